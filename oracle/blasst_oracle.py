@@ -1,0 +1,298 @@
+"""Plain CPU oracle for BLASST skip-softmax attention.
+
+TEST INFRASTRUCTURE ONLY. Only the test suite, the package's smoke entry and
+the benchmark's CPU-baseline leg may import this module. The GPU path neither
+imports it nor shares any code with it, and this module imports nothing from
+the GPU path.
+
+What is computed (sources are the BLASST explainer post "BLASST: Dynamic
+BLocked Attention Sparsity via Softmax Thresholding" on the seeallochnaya
+Telegram channel, called "the BLASST post" below, and the digg.com thread
+"BLASST wins Best Paper at MLSys 2026 ...", called "the digg thread"):
+
+* Attention is computed block by block along the keys, in increasing key
+  order, with the usual max-subtracted (shift-invariant) softmax
+  (BLASST post, paragraph "В чём идея").
+* The maximum is tracked online: a running per-row maximum is compared with
+  each new block's maximum, and earlier partial sums are rescaled when it
+  grows; after the last block the result is exact (BLASST post, paragraph on
+  the online trick of FlashAttention 1).
+* BLASST: when a block's maximum is far below the maximum of the blocks
+  before it, the whole block is dropped, and its V rows take no part in the
+  result (BLASST post, paragraph beginning "BLASST предлагает"). The first block
+  is always processed (BLASST post, first figure). The test is a single scalar
+  threshold on the online softmax statistics, reusing the running max (digg
+  thread, the authors' posts).
+
+Readings taken where the pages are silent (each one is listed in the design
+notes of the repository):
+
+* thr = ln(lambda) in the natural-log units of the scaled logits
+  s = scale * q.k; lambda = 0 means thr = -inf (nothing dropped); lambda must
+  lie in [0, 1].
+* A tile's gap is the maximum over its valid rows of (row max in the tile
+  minus the row's running max), so a tile is dropped only when *every* row is
+  below the threshold; the comparison is strict (a tie keeps the tile).
+* A row with no visible key in the tile votes "drop" (gap -inf); a row whose
+  running max is still -inf votes "keep" (gap +inf).
+* Causal masking is bottom-right aligned: query i sits at key position
+  Nk - Nq + i. Tiles with no visible (row, key) pair at all are "not visited"
+  (mask value 2) and are not counted as dropped.
+* GQA: query head h reads key/value head h // (Hq / Hkv).
+* Decode is the same rule with one query row per (batch, head); tile 0 is
+  the global first key tile and the running max is global along the keys.
+
+Arithmetic is float64 throughout; inputs are whatever float values the caller
+passes (bf16 workloads pass the exact bf16 values, widened).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+MASK_SKIPPED = 0
+MASK_KEPT = 1
+MASK_NOT_VISITED = 2
+
+
+def threshold(lam: float) -> float:
+    """thr = ln(lambda), with ln(0) = -inf. lambda must be in [0, 1]."""
+    lam = float(lam)
+    if not (0.0 <= lam <= 1.0):
+        raise ValueError(f"lambda must lie in [0, 1], got {lam!r}")
+    return -math.inf if lam == 0.0 else math.log(lam)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def visible(nq: int, nk: int, causal: bool, row0: int = 0, rows: Optional[int] = None) -> np.ndarray:
+    """Boolean [rows, nk]: may query (row0 + r) see key c? Bottom-right causal alignment."""
+    if rows is None:
+        rows = nq - row0
+    r = np.arange(row0, row0 + rows)[:, None]
+    c = np.arange(nk)[None, :]
+    if not causal:
+        return np.ones((rows, nk), dtype=bool)
+    return c <= r + (nk - nq)
+
+
+@dataclass
+class TileRowResult:
+    out: np.ndarray       # [rows, dv]
+    lse: np.ndarray       # [rows]
+    mask: np.ndarray      # [nKt] uint8: 0 dropped, 1 kept, 2 not visited
+    gap: np.ndarray       # [nKt] float64 tile max-gap (nan where not visited)
+    m_before: np.ndarray  # [nKt, rows] running max on entry to each tile (-inf before tile 0)
+    tile_max: np.ndarray  # [nKt, rows] row max inside each tile (-inf where none visible)
+
+
+def blasst_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, lam: float, bc: int,
+                vis: np.ndarray, scale: float) -> TileRowResult:
+    """The ordered skip rule for one block of query rows against one key/value head.
+
+    q: [rows, d] query rows that form one query tile; k: [Nk, d]; v: [Nk, dv];
+    vis: [rows, Nk] visibility. Key tiles are visited left to right.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    rows, nk = vis.shape
+    dv = v.shape[1]
+    thr = threshold(lam)
+    nkt = -(-nk // bc)
+
+    # scores of this query tile against every key, masked entries at -inf
+    s = scale * (q @ k.T)
+    s = np.where(vis, s, -np.inf)
+
+    m = np.full(rows, -np.inf)
+    l = np.zeros(rows)
+    o = np.zeros((rows, dv))
+    mask = np.full(nkt, MASK_NOT_VISITED, dtype=np.uint8)
+    gap = np.full(nkt, np.nan)
+    m_before = np.full((nkt, rows), -np.inf)
+    tile_max = np.full((nkt, rows), -np.inf)
+
+    for j in range(nkt):
+        c0, c1 = j * bc, min((j + 1) * bc, nk)
+        if not vis[:, c0:c1].any():
+            continue  # no visible (row, key) pair: the tile is not visited
+        st = s[:, c0:c1]
+        mt = st.max(axis=1)
+        m_before[j] = m
+        tile_max[j] = mt
+        # per-row gap with the infinity conventions, then the tile's max-gap
+        g_r = np.where(mt == -np.inf, -np.inf, np.where(m == -np.inf, np.inf, mt - m))
+        g = g_r.max() if rows else -np.inf
+        gap[j] = g
+        keep = (j == 0) or not (g < thr)
+        if not keep:
+            mask[j] = MASK_SKIPPED
+            continue
+        mask[j] = MASK_KEPT
+        m_new = np.maximum(m, mt)
+        alpha = np.exp(m - m_new)       # 0 where m was -inf
+        p = np.exp(st - m_new[:, None])  # 0 where masked
+        l = alpha * l + p.sum(axis=1)
+        o = alpha[:, None] * o + p @ v[c0:c1]
+        m = m_new
+
+    with np.errstate(divide="ignore", invalid="ignore"):
+        out = o / l[:, None]
+        lse = m + np.log(l)
+    return TileRowResult(out, lse, mask, gap, m_before, tile_max)
+
+
+@dataclass
+class OracleResult:
+    out: np.ndarray    # prefill [B,Hq,Nq,dv] / decode [B,Hq,dv]
+    lse: np.ndarray    # prefill [B,Hq,Nq] / decode [B,Hq]
+    mask: np.ndarray   # prefill [B,Hq,nQt,nKt] / decode [B,Hq,nKt]
+    gap: np.ndarray    # same shape as mask
+    stats: np.ndarray  # prefill [B,Hq,2] = (visited, kept); decode [B,Hq,3] adds V tiles loaded
+
+
+def prefill_tile(q: np.ndarray, k: np.ndarray, v: np.ndarray, b: int, hq: int, i: int,
+                 lam: float, causal: bool, br: int, bc: int,
+                 scale: Optional[float] = None) -> TileRowResult:
+    """One (batch b, query head hq, query tile i) of a prefill call.
+
+    q: [B,Hq,Nq,d]; k: [B,Hkv,Nk,d]; v: [B,Hkv,Nk,dv].
+    """
+    B, Hq, nq, d = q.shape
+    hkv = k.shape[1]
+    if Hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    kvh = hq // (Hq // hkv)
+    nk = k.shape[2]
+    if scale is None:
+        scale = default_scale(d)
+    r0, r1 = i * br, min((i + 1) * br, nq)
+    vis = visible(nq, nk, causal, r0, r1 - r0)
+    return blasst_rows(q[b, hq, r0:r1], k[b, kvh], v[b, kvh], lam, bc, vis, scale)
+
+
+def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, lam: float, causal: bool,
+            br: int, bc: int, scale: Optional[float] = None) -> OracleResult:
+    """Whole prefill call: every (b, hq, query tile) independently."""
+    B, Hq, nq, d = q.shape
+    nk, dv = k.shape[2], v.shape[3]
+    if causal and nq > nk:
+        raise ValueError("causal prefill needs Nq <= Nk")
+    nqt, nkt = -(-nq // br), -(-nk // bc)
+    out = np.zeros((B, Hq, nq, dv))
+    lse = np.zeros((B, Hq, nq))
+    mask = np.full((B, Hq, nqt, nkt), MASK_NOT_VISITED, dtype=np.uint8)
+    gap = np.full((B, Hq, nqt, nkt), np.nan)
+    stats = np.zeros((B, Hq, 2), dtype=np.int64)
+    for b in range(B):
+        for hq in range(Hq):
+            for i in range(nqt):
+                r = prefill_tile(q, k, v, b, hq, i, lam, causal, br, bc, scale)
+                r0 = i * br
+                out[b, hq, r0:r0 + r.out.shape[0]] = r.out
+                lse[b, hq, r0:r0 + r.out.shape[0]] = r.lse
+                mask[b, hq, i] = r.mask
+                gap[b, hq, i] = r.gap
+            stats[b, hq, 0] = int((mask[b, hq] != MASK_NOT_VISITED).sum())
+            stats[b, hq, 1] = int((mask[b, hq] == MASK_KEPT).sum())
+    return OracleResult(out, lse, mask, gap, stats)
+
+
+def decode_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, b: int, hq: int,
+               lam: float, bc: int, scale: Optional[float] = None) -> TileRowResult:
+    """One (batch b, query head hq) decode row: a single query that sees every key.
+
+    q: [B,Hq,d]; k: [B,Hkv,Nk,d]; v: [B,Hkv,Nk,dv] (for an MLA latent cache pass
+    ``k[..., :dv]``).
+    """
+    B, Hq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    kvh = hq // (Hq // hkv)
+    if scale is None:
+        scale = default_scale(d)
+    return blasst_rows(q[b, hq][None, :], k[b, kvh], v[b, kvh], lam, bc,
+                       np.ones((1, nk), dtype=bool), scale)
+
+
+def decode(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], lam: float, bc: int,
+           scale: Optional[float] = None, dv: Optional[int] = None) -> OracleResult:
+    """Whole decode call. With ``v`` None the values are ``k[..., :dv]`` (MLA)."""
+    B, Hq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    G = Hq // hkv
+    if v is None:
+        if dv is None:
+            raise ValueError("dv is required when V is a slice of K")
+        v = k[..., :dv]
+    dv = v.shape[3]
+    nkt = -(-nk // bc)
+    out = np.zeros((B, Hq, dv))
+    lse = np.zeros((B, Hq))
+    mask = np.zeros((B, Hq, nkt), dtype=np.uint8)
+    gap = np.zeros((B, Hq, nkt))
+    stats = np.zeros((B, Hq, 3), dtype=np.int64)
+    for b in range(B):
+        for hq in range(Hq):
+            r = decode_row(q, k, v, b, hq, lam, bc, scale)
+            out[b, hq] = r.out[0]
+            lse[b, hq] = r.lse[0]
+            mask[b, hq] = r.mask
+            gap[b, hq] = r.gap
+        for g0 in range(0, Hq, G):
+            # a V tile is fetched for a KV head when any query head that reads it keeps it
+            loaded = int((mask[b, g0:g0 + G] == MASK_KEPT).any(axis=0).sum())
+            stats[b, g0:g0 + G, 2] = loaded
+        stats[b, :, 0] = nkt
+        stats[b, :, 1] = (mask[b] == MASK_KEPT).sum(axis=1)
+    return OracleResult(out, lse, mask, gap, stats)
+
+
+def naive_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
+                    scale: Optional[float] = None) -> np.ndarray:
+    """Textbook softmax(scale * q k^T) v for one head: q [Nq,d], k [Nk,d], v [Nk,dv]."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    if scale is None:
+        scale = default_scale(q.shape[1])
+    s = scale * (q @ k.T)
+    s = np.where(visible(q.shape[0], k.shape[0], causal), s, -np.inf)
+    s = s - s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p @ v) / p.sum(axis=1, keepdims=True)
+
+
+def expand_tile_mask(mask_row: np.ndarray, br: int, bc: int, nq: int, nk: int) -> np.ndarray:
+    """[nQt, nKt] tile mask -> [nq, nk] boolean 'kept' per (query, key) pair."""
+    kept = (np.asarray(mask_row) == MASK_KEPT)
+    el = np.repeat(np.repeat(kept, br, axis=0), bc, axis=1)
+    return el[:nq, :nk]
+
+
+def masked_dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np.ndarray,
+                           causal: bool, scale: Optional[float] = None) -> tuple:
+    """Softmax attention restricted to the kept keys (numerator and denominator).
+
+    One head: q [Nq,d], k [Nk,d], v [Nk,dv], keep [Nq,Nk] boolean. Returns (out, lse).
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    if scale is None:
+        scale = default_scale(q.shape[1])
+    s = scale * (q @ k.T)
+    allowed = keep & visible(q.shape[0], k.shape[0], causal)
+    s = np.where(allowed, s, -np.inf)
+    mx = s.max(axis=1, keepdims=True)
+    p = np.exp(s - mx)
+    den = p.sum(axis=1, keepdims=True)
+    return (p @ v) / den, (mx + np.log(den))[:, 0]
+
+
+__all__ = [
+    "threshold", "default_scale", "visible", "blasst_rows", "prefill_tile", "prefill",
+    "decode_row", "decode", "naive_attention", "expand_tile_mask", "masked_dense_attention",
+    "OracleResult", "TileRowResult", "MASK_SKIPPED", "MASK_KEPT", "MASK_NOT_VISITED",
+]

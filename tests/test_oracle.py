@@ -1,0 +1,443 @@
+"""Pins for the CPU oracle (no GPU).
+
+Each ``pin_*`` function checks the oracle against something other than
+itself: hand-derived fixtures under tests/golden, torch's CPU
+scaled_dot_product_attention in float64, the closed form implied by the
+prefix-max invariant, and a from-definition brute force. The mutation tests
+at the bottom plant plausible mistakes in a copy of the oracle's source and
+check that at least one pin catches each of them.
+"""
+import importlib.util
+import json
+import math
+import os
+import sys
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_long_skip_amd import synth
+
+GOLD = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLD, name)) as f:
+        return json.load(f)
+
+
+def _f(x):
+    return float(x) if not isinstance(x, str) else float(x.replace("inf", "inf"))
+
+
+def _rand_case(rng, B, Hq, Hkv, Nq, Nk, d, dv, plant=0.0):
+    q = rng.standard_normal((B, Hq, Nq, d))
+    k = rng.standard_normal((B, Hkv, Nk, d))
+    v = rng.standard_normal((B, Hkv, Nk, dv))
+    if plant:
+        u = rng.standard_normal(d)
+        u /= np.linalg.norm(u)
+        q += plant * u
+        idx = rng.choice(Nk, size=max(1, Nk // 12), replace=False)
+        k[:, :, idx] += plant * u
+        k[:, :, 0] += plant * u
+    return q, k, v
+
+
+def _sdpa(q, k, v, causal, scale, attn_mask=None):
+    """torch CPU float64 reference for one head or a batch of heads."""
+    tq, tk, tv = (torch.from_numpy(np.ascontiguousarray(x)) for x in (q, k, v))
+    m = None if attn_mask is None else torch.from_numpy(attn_mask)
+    return torch.nn.functional.scaled_dot_product_attention(
+        tq, tk, tv, attn_mask=m, is_causal=causal and attn_mask is None, scale=scale).numpy()
+
+
+# --------------------------------------------------------------------------- pins
+
+def pin_hand_example(orc):
+    g = _load("hand_example.json")
+    sh = g["shape"]
+    q = np.array(g["q"])[None, None]
+    k = np.array(g["k"])[None, None]
+    v = np.array(g["v"])[None, None]
+    for case in g["cases"]:
+        lam = math.exp(case["log_lambda"]) if case["log_lambda"] != "-inf" else 0.0
+        r = orc.prefill(q, k, v, lam, sh["causal"], sh["br"], sh["bc"], scale=sh["scale"])
+        assert r.mask[0, 0, 0].tolist() == case["mask"]
+        assert np.allclose(r.gap[0, 0, 0], [_f(x) for x in case["gap"]], rtol=0, atol=1e-12)
+        ks = np.array(case["out_terms"]["kept_scores"])
+        kv = np.array(case["out_terms"]["kept_values"])
+        # closed form: softmax over the kept keys only
+        want_out = float((np.exp(ks) * kv).sum() / np.exp(ks).sum())
+        want_lse = float(np.log(np.exp(ks).sum()))
+        assert abs(r.out[0, 0, 0, 0] - want_out) < 1e-12
+        assert abs(r.lse[0, 0, 0] - want_lse) < 1e-12
+    # the survey's printed digits for the first case
+    assert abs((1 + 3 * math.e) / (1 + math.e) - 2.4621171573) < 1e-10
+
+
+def pin_row_aggregation(orc):
+    g = _load("row_aggregation.json")
+    sh = g["shape"]
+    q = np.array(g["q"])[None, None]
+    for case in g["cases"]:
+        k = np.array(case["k"])[None, None]
+        v = np.arange(sh["Nk"], dtype=np.float64).reshape(1, 1, sh["Nk"], 1)
+        r = orc.prefill(q, k, v, g["lambda"], sh["causal"], sh["br"], sh["bc"], scale=sh["scale"])
+        assert r.mask[0, 0, 0].tolist() == case["mask"], case["derivation"]
+        assert np.allclose(r.gap[0, 0, 0], [_f(x) for x in case["gap"]])
+
+
+def pin_tie(orc):
+    g = _load("tie.json")
+    q = np.array(g["q"])[None, None]
+    for case in g["cases"]:
+        k = np.array(case["k"])[None, None]
+        v = np.array(case["v"])[None, None]
+        r = orc.prefill(q, k, v, g["lambda"], False, 1, 1, scale=1.0)
+        assert r.mask[0, 0, 0].tolist() == case["mask"], case["derivation"]
+        if "out" in case:
+            assert abs(r.out[0, 0, 0, 0] - case["out"]) < 1e-12
+
+
+def pin_causal_visibility(orc):
+    g = _load("causal_visibility.json")
+    sh = g["shape"]
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((1, 1, sh["Nq"], 1))
+    k = rng.standard_normal((1, 1, sh["Nk"], 1))
+    v = rng.standard_normal((1, 1, sh["Nk"], 1))
+    r = orc.prefill(q, k, v, 0.0, True, sh["br"], sh["bc"], scale=1.0)
+    assert r.mask[0, 0].tolist() == g["expect"]["mask_lambda0"]
+
+
+def pin_lambda0_sdpa(orc):
+    """lambda = 0 drops nothing: equals textbook softmax attention (torch SDPA, float64)."""
+    rng = np.random.default_rng(1)
+    for (B, Hq, Hkv, N, d, dv, br, bc, causal) in [
+        (1, 2, 2, 37, 8, 8, 8, 4, True),
+        (2, 4, 2, 53, 16, 12, 16, 8, True),   # GQA, dv != d, ragged
+        (1, 6, 3, 40, 4, 4, 5, 7, False),
+        (1, 3, 1, 129, 8, 8, 128, 64, True),  # the bf16 kernel's tiling, ragged tail
+    ]:
+        q, k, v = _rand_case(rng, B, Hq, Hkv, N, N, d, dv)
+        sc = 1.0 / math.sqrt(d)
+        r = orc.prefill(q, k, v, 0.0, causal, br, bc)
+        G = Hq // Hkv
+        kk = np.repeat(k, G, axis=1)  # q head h reads kv head h // G
+        vv = np.repeat(v, G, axis=1)
+        ref = _sdpa(q, kk, vv, causal, sc)
+        assert np.abs(r.out - ref).max() < 1e-12
+        # lse against logsumexp of the visible scores
+        s = sc * np.einsum("bhqd,bhkd->bhqk", q, kk)
+        if causal:
+            s = np.where(np.tril(np.ones((N, N), dtype=bool)), s, -np.inf)
+        ref_lse = torch.logsumexp(torch.from_numpy(s), dim=-1).numpy()
+        assert np.abs(r.lse - ref_lse).max() < 1e-12
+        assert (r.mask[r.mask != 2] == 1).all()
+
+
+def pin_bottom_right_causal(orc):
+    """Causal with Nq < Nk equals the last Nq rows of the square causal problem."""
+    rng = np.random.default_rng(2)
+    Nk, Nq, d = 45, 13, 8
+    qfull, k, v = _rand_case(rng, 1, 1, 1, Nk, Nk, d, d)
+    ref = _sdpa(qfull, k, v, True, 1.0 / math.sqrt(d))[:, :, Nk - Nq:]
+    r = orc.prefill(qfull[:, :, Nk - Nq:], k, v, 0.0, True, 4, 8)
+    assert np.abs(r.out - ref).max() < 1e-12
+
+
+def pin_masked_sdpa(orc):
+    """lambda > 0: the output is softmax attention restricted to the kept tiles."""
+    rng = np.random.default_rng(3)
+    n_skipped = 0
+    for (B, Hq, Hkv, Nq, Nk, d, br, bc, causal, lam) in [
+        (1, 2, 1, 70, 70, 16, 8, 4, True, 1e-2),
+        (1, 2, 2, 33, 90, 8, 4, 8, True, 1e-1),
+        (2, 2, 1, 25, 64, 8, 5, 3, False, 1e-3),
+    ]:
+        q, k, v = _rand_case(rng, B, Hq, Hkv, Nq, Nk, d, d, plant=6.0)
+        sc = 1.0 / math.sqrt(d)
+        r = orc.prefill(q, k, v, lam, causal, br, bc)
+        n_skipped += int((r.mask == 0).sum())
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                keep = orc.expand_tile_mask(r.mask[b, h], br, bc, Nq, Nk)
+                r_idx = np.arange(Nq)[:, None] + (Nk - Nq)
+                vis = (np.arange(Nk)[None, :] <= r_idx) if causal else np.ones((Nq, Nk), bool)
+                am = keep & vis
+                ref = _sdpa(q[b, h][None], k[b, h // G][None], v[b, h // G][None], False, sc,
+                            attn_mask=am[None])
+                assert np.abs(r.out[b, h] - ref[0]).max() < 1e-12
+    assert n_skipped > 0, "fixture must exercise dropped tiles"
+
+
+def _prefix_max_closed_form(q, k, lam, causal, br, bc, scale):
+    """mask[i,j] = j==0 or max_r (tilemax[r,j] - max_{t<j} tilemax[r,t]) >= thr, from dense S."""
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk = k.shape[1], k.shape[2]
+    G = Hq // Hkv
+    thr = -np.inf if lam == 0 else np.log(lam)
+    nqt, nkt = -(-Nq // br), -(-Nk // bc)
+    out = np.full((B, Hq, nqt, nkt), 2, dtype=np.uint8)
+    for b in range(B):
+        for h in range(Hq):
+            s = scale * q[b, h] @ k[b, h // G].T
+            if causal:
+                s = np.where(np.arange(Nk)[None] <= np.arange(Nq)[:, None] + Nk - Nq, s, -np.inf)
+            # pad to whole tiles with -inf, then per-(row, tile) maxima
+            sp = np.full((nqt * br, nkt * bc), -np.inf)
+            sp[:Nq, :Nk] = s
+            tm = sp.reshape(nqt, br, nkt, bc).max(axis=3)  # [nqt, br, nkt]
+            pm = np.maximum.accumulate(tm, axis=2)
+            prev = np.concatenate([np.full((nqt, br, 1), -np.inf), pm[:, :, :-1]], axis=2)
+            with np.errstate(invalid="ignore"):
+                gap = np.where(tm == -np.inf, -np.inf, np.where(prev == -np.inf, np.inf, tm - prev))
+            g = gap.max(axis=1)  # over rows (padding rows are all -inf)
+            visited = (tm > -np.inf).any(axis=1)
+            keep = (np.arange(nkt)[None] == 0) | ~(g < thr)
+            out[b, h] = np.where(visited, keep.astype(np.uint8), 2)
+    return out
+
+
+def pin_closed_form_mask(orc):
+    rng = np.random.default_rng(4)
+    for (Hq, Hkv, Nq, Nk, d, br, bc, causal) in [
+        (2, 1, 96, 96, 8, 16, 8, True), (2, 2, 40, 77, 4, 8, 5, True), (3, 3, 31, 50, 8, 6, 4, False),
+    ]:
+        q, k, v = _rand_case(rng, 1, Hq, Hkv, Nq, Nk, d, d, plant=5.0)
+        for lam in (0.0, 1e-4, 1e-2, 0.2, 1.0):
+            r = orc.prefill(q, k, v, lam, causal, br, bc)
+            cf = _prefix_max_closed_form(q, k, lam, causal, br, bc, 1 / math.sqrt(d))
+            assert (r.mask == cf).all(), (lam, causal)
+
+
+def _brute(q, k, v, lam, causal, br, bc, scale):
+    """Pure-Python loops straight from the definition, no incremental state.
+
+    The running max before tile j is recomputed from scratch as the max score
+    over the tiles kept so far; the output is a plain softmax over kept keys.
+    """
+    Nq, d = len(q), len(q[0])
+    Nk = len(k)
+    thr = -math.inf if lam == 0 else math.log(lam)
+    nqt, nkt = -(-Nq // br), -(-Nk // bc)
+
+    def score(r, c):
+        return scale * sum(q[r][x] * k[c][x] for x in range(d))
+
+    def vis(r, c):
+        return (not causal) or c <= r + Nk - Nq
+
+    mask = [[2] * nkt for _ in range(nqt)]
+    out = [[0.0] * len(v[0]) for _ in range(Nq)]
+    for i in range(nqt):
+        rows = range(i * br, min((i + 1) * br, Nq))
+        kept = []
+        for j in range(nkt):
+            cols = range(j * bc, min((j + 1) * bc, Nk))
+            if not any(vis(r, c) for r in rows for c in cols):
+                continue
+            gaps = []
+            for r in rows:
+                vals = [score(r, c) for c in cols if vis(r, c)]
+                if not vals:
+                    gaps.append(-math.inf)
+                    continue
+                prev = [score(r, c) for t in kept for c in range(t * bc, min((t + 1) * bc, Nk))
+                        if vis(r, c)]
+                gaps.append(math.inf if not prev else max(vals) - max(prev))
+            g = max(gaps)
+            if j == 0 or not (g < thr):
+                kept.append(j)
+                mask[i][j] = 1
+            else:
+                mask[i][j] = 0
+        for r in rows:
+            cs = [c for t in kept for c in range(t * bc, min((t + 1) * bc, Nk)) if vis(r, c)]
+            mx = max(score(r, c) for c in cs)
+            w = [math.exp(score(r, c) - mx) for c in cs]
+            den = sum(w)
+            for x in range(len(v[0])):
+                out[r][x] = sum(wi * v[c][x] for wi, c in zip(w, cs)) / den
+    return mask, out
+
+
+def pin_brute_force(orc):
+    rng = np.random.default_rng(5)
+    for trial in range(24):
+        Nq = int(rng.integers(1, 13))
+        Nk = int(rng.integers(Nq, 17))
+        d = int(rng.choice([1, 2, 4]))
+        br = int(rng.choice([1, 2, 4]))
+        bc = int(rng.choice([1, 2, 4]))
+        causal = bool(rng.integers(0, 2))
+        lam = float(rng.choice([0.0, 1e-3, 0.05, 0.3, 1.0]))
+        q, k, v = _rand_case(rng, 1, 1, 1, Nq, Nk, d, 2, plant=float(rng.choice([0.0, 3.0])))
+        sc = 1.0 / math.sqrt(d)
+        r = orc.prefill(q, k, v, lam, causal, br, bc)
+        bm, bo = _brute(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), lam, causal, br, bc, sc)
+        assert r.mask[0, 0].tolist() == bm, trial
+        assert np.abs(r.out[0, 0] - np.array(bo)).max() < 1e-12, trial
+
+
+def pin_decode_sdpa(orc):
+    """Decode at lambda 0 (plain GQA and MLA latent layout) equals softmax attention."""
+    rng = np.random.default_rng(6)
+    B, Hq, Hkv, Nk, d = 2, 8, 2, 150, 16
+    q = rng.standard_normal((B, Hq, d))
+    k = rng.standard_normal((B, Hkv, Nk, d))
+    v = rng.standard_normal((B, Hkv, Nk, d))
+    r = orc.decode(q, k, v, 0.0, 64)
+    G = Hq // Hkv
+    ref = _sdpa(q[:, :, None], np.repeat(k, G, 1), np.repeat(v, G, 1), False, 1 / math.sqrt(d))
+    assert np.abs(r.out - ref[:, :, 0]).max() < 1e-12
+    # MLA: one latent head, V = first dv columns of K
+    km = rng.standard_normal((B, 1, Nk, 24))
+    qm = rng.standard_normal((B, 4, 24))
+    rm = orc.decode(qm, km, None, 0.0, 64, dv=16)
+    refm = _sdpa(qm[:, :, None], np.repeat(km, 4, 1), np.repeat(km[..., :16], 4, 1), False,
+                 1 / math.sqrt(24))
+    assert np.abs(rm.out - refm[:, :, 0]).max() < 1e-12
+
+
+PINS = [pin_hand_example, pin_row_aggregation, pin_tie, pin_causal_visibility,
+        pin_lambda0_sdpa, pin_bottom_right_causal, pin_masked_sdpa, pin_closed_form_mask,
+        pin_brute_force, pin_decode_sdpa]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
+def test_pin(pin):
+    pin(oracle)
+
+
+# --------------------------------------------------------------------------- invariants
+
+def test_threshold_domain():
+    assert oracle.threshold(0.0) == -math.inf
+    assert oracle.threshold(1.0) == 0.0
+    assert abs(oracle.threshold(1e-3) - math.log(1e-3)) < 1e-15
+    for bad in (-1e-9, 1.0000001, float("nan"), 2.0):
+        with pytest.raises(ValueError):
+            oracle.threshold(bad)
+
+
+def test_prefix_max_invariant_and_nesting():
+    """For lambda <= 1 a dropped tile can never raise the running max, so the
+    running max on entry to tile j is the plain prefix max; kept sets are nested
+    in lambda and tile 0 is always kept."""
+    rng = np.random.default_rng(7)
+    q, k, v = _rand_case(rng, 1, 2, 1, 64, 200, 8, 8, plant=6.0)
+    lams = [0.0, 1e-6, 1e-4, 1e-3, 1e-2, 0.1, 1.0]
+    prev_kept = None
+    fracs = []
+    for lam in lams:
+        kept_all = []
+        for h in range(2):
+            for i in range(4):
+                t = oracle.prefill_tile(q, k, v, 0, h, i, lam, True, 16, 8)
+                vis_t = t.mask != 2
+                pm = np.maximum.accumulate(t.tile_max, axis=0)
+                prev = np.vstack([np.full((1, pm.shape[1]), -np.inf), pm[:-1]])
+                assert np.array_equal(t.m_before[vis_t], prev[vis_t])
+                assert t.mask[0] == 1
+                kept_all.append(t.mask == 1)
+        kept = np.concatenate(kept_all)
+        if prev_kept is not None:
+            assert not (kept & ~prev_kept).any(), "kept sets must be nested in lambda"
+        prev_kept = kept
+        fracs.append(1 - kept.sum() / len(kept))
+    assert all(a <= b for a, b in zip(fracs, fracs[1:]))
+    assert fracs[-1] > 0.2
+
+
+def test_stats_consistency():
+    rng = np.random.default_rng(8)
+    q, k, v = _rand_case(rng, 2, 4, 2, 50, 50, 8, 8, plant=6.0)
+    r = oracle.prefill(q, k, v, 1e-2, True, 8, 8)
+    assert (r.stats[..., 0] == (r.mask != 2).sum(axis=(2, 3))).all()
+    assert (r.stats[..., 1] == (r.mask == 1).sum(axis=(2, 3))).all()
+    qd = rng.standard_normal((2, 4, 8)) + 3
+    rd = oracle.decode(qd, k, v, 1e-2, 8)
+    G = 2
+    for b in range(2):
+        for h in range(4):
+            grp = rd.mask[b, (h // G) * G:(h // G + 1) * G]
+            assert rd.stats[b, h, 2] == (grp == 1).any(axis=0).sum()
+
+
+def test_decode_equals_prefill_with_one_row():
+    rng = np.random.default_rng(9)
+    B, Hq, Hkv, Nk, d = 1, 4, 2, 70, 8
+    q = rng.standard_normal((B, Hq, d)) + 2.0
+    k, v = rng.standard_normal((B, Hkv, Nk, d)), rng.standard_normal((B, Hkv, Nk, d))
+    k[:, :, ::9] += 3.0
+    for lam in (0.0, 1e-2, 0.5):
+        rd = oracle.decode(q, k, v, lam, 8)
+        rp = oracle.prefill(q[:, :, None], k, v, lam, False, 1, 8)
+        assert np.array_equal(rd.mask, rp.mask[:, :, 0])
+        assert np.abs(rd.out - rp.out[:, :, 0]).max() == 0
+
+
+def test_generator_workload_skips_only_with_gain():
+    """The workloads as specified plant boosts too weak to cross ln(lambda); the
+    supplementary gain makes dropped tiles appear (recorded in the design notes)."""
+    w = synth.small_workload("prefill", Hq=1, Hkv=1, Nq=256, Nk=1024, d=64, dtype="fp32",
+                             br=64, bc=64, seed=11, window=0)
+    for gain, expect_skip in ((1.0, False), (6.0, True)):
+        inp = synth.make_inputs(w.with_gain(gain))
+        q, k, v = (synth.to_float(x, w) for x in (inp.q, inp.k, inp.v))
+        r = oracle.prefill(q, k, v, 1e-2, True, 64, 64)
+        assert bool((r.mask == 0).any()) == expect_skip
+
+
+# --------------------------------------------------------------------------- mutation tests
+
+_SRC = open(os.path.join(os.path.dirname(oracle.__file__), "blasst_oracle.py")).read()
+
+MUTATIONS = {
+    "any_row_instead_of_all_rows": ("g = g_r.max() if rows else -np.inf", "g = g_r.min() if rows else -np.inf"),
+    "non_strict_threshold": ("keep = (j == 0) or not (g < thr)", "keep = (j == 0) or not (g <= thr)"),
+    "dropped_rescale_of_l": ("l = alpha * l + p.sum(axis=1)", "l = l + p.sum(axis=1)"),
+    "dropped_rescale_of_o": ("o = alpha[:, None] * o + p @ v[c0:c1]", "o = o + p @ v[c0:c1]"),
+    "gqa_modulo_mapping": ("kvh = hq // (Hq // hkv)\n    nk = k.shape[2]", "kvh = hq % hkv\n    nk = k.shape[2]"),
+    "top_left_causal": ("return c <= r + (nk - nq)", "return c <= r"),
+    "gap_sign_flipped": ("np.where(m == -np.inf, np.inf, mt - m)", "np.where(m == -np.inf, np.inf, m - mt)"),
+    "missing_scale": ("s = scale * (q @ k.T)\n    s = np.where(vis", "s = (q @ k.T)\n    s = np.where(vis"),
+    "running_max_not_updated": ("        m = m_new\n", "        m = np.maximum(m, 0 * m_new)\n"),
+    "first_tile_not_forced": ("keep = (j == 0) or not (g < thr)", "keep = not (g < thr) and j >= 0"),
+    "threshold_log10": ("math.log(lam)", "math.log10(lam)"),
+}
+
+
+def _mutant(old, new):
+    assert old in _SRC, f"mutation anchor missing: {old!r}"
+    src = _SRC.replace(old, new)
+    mod = types.ModuleType("oracle_mutant")
+    mod.__dict__["__name__"] = "oracle_mutant"
+    sys.modules["oracle_mutant"] = mod
+    exec(compile(src, "oracle_mutant.py", "exec"), mod.__dict__)
+    return mod
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_planted_mistake(name):
+    old, new = MUTATIONS[name]
+    mut = _mutant(old, new)
+    caught = []
+    for pin in PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(mut)
+        except Exception:  # noqa: BLE001 - any failure means the pin caught it
+            caught.append(pin.__name__)
+    # "first tile not forced" is benign: tile 0 always has gap +inf, so the
+    # convention already keeps it. Every other mutation must be caught.
+    if name == "first_tile_not_forced":
+        assert caught == []
+    else:
+        assert caught, f"no pin caught mutation {name}"

@@ -1,0 +1,198 @@
+"""Thin ctypes binding over libblasst (include/blasst.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libblasst.so. PyTorch provides device memory (output tensors are
+allocated with ``torch.empty`` on the input's device) and the stream
+(``torch.cuda.current_stream()``). There is no CPU fallback: if the library
+is missing or a call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libblasst.so")
+
+BLASST_FP32 = 0
+BLASST_BF16 = 1
+
+STATUS = {
+    0: "BLASST_OK", 1: "BLASST_E_NULL", 2: "BLASST_E_SHAPE", 3: "BLASST_E_DTYPE",
+    4: "BLASST_E_LAMBDA", 5: "BLASST_E_ALIGN", 6: "BLASST_E_UNSUPPORTED", 7: "BLASST_E_ARG",
+    8: "BLASST_E_HIP",
+}
+
+# Every symbol include/blasst.h declares.
+EXPORTED = ("blasst_attn_prefill", "blasst_attn_decode", "blasst_status_string",
+            "blasst_last_error", "blasst_version")
+
+
+class Shape(ctypes.Structure):
+    """blasst_shape_t."""
+
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads_q", ctypes.c_int32), ("heads_kv", ctypes.c_int32),
+        ("len_q", ctypes.c_int32), ("len_kv", ctypes.c_int32), ("d_qk", ctypes.c_int32),
+        ("d_v", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class BlasstError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libblasst.so once and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m block_sparse_long_skip_amd.build` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    vp, i64p, u8p, fp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
+    lib.blasst_attn_prefill.restype = ctypes.c_int
+    lib.blasst_attn_prefill.argtypes = [vp, vp, vp, vp, u8p, fp, i64p, ctypes.POINTER(Shape),
+                                        ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+    lib.blasst_attn_decode.restype = ctypes.c_int
+    lib.blasst_attn_decode.argtypes = [vp, vp, vp, vp, u8p, fp, i64p, ctypes.POINTER(Shape),
+                                       ctypes.c_int, ctypes.c_float, ctypes.c_float,
+                                       ctypes.c_int, vp]
+    lib.blasst_status_string.restype = ctypes.c_char_p
+    lib.blasst_status_string.argtypes = [ctypes.c_int]
+    lib.blasst_last_error.restype = ctypes.c_char_p
+    lib.blasst_last_error.argtypes = []
+    lib.blasst_version.restype = ctypes.c_int
+    lib.blasst_version.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        detail = load_library().blasst_last_error().decode(errors="replace")
+        raise BlasstError(status, detail)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return BLASST_FP32
+    if t.dtype == torch.bfloat16:
+        return BLASST_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _strides3(t: torch.Tensor):
+    if t.stride(-1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+    s = t.stride()
+    return (s[0], s[1], s[2]) if t.dim() == 4 else (s[0], s[1], 0)
+
+
+def _stream(dev: torch.device) -> int:
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _require_device(*ts: Optional[torch.Tensor]) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libblasst runs on the GPU only: every tensor must be on a HIP device")
+
+
+@dataclass
+class AttnResult:
+    out: torch.Tensor
+    mask: Optional[torch.Tensor]
+    lse: Optional[torch.Tensor]
+    stats: Optional[torch.Tensor]
+
+    @property
+    def skip_fraction(self) -> float:
+        """Dropped / visited key tiles over the whole call (needs stats)."""
+        st = self.stats.double()
+        visited = st[..., 0].sum().item()
+        return 0.0 if visited == 0 else 1.0 - st[..., 1].sum().item() / visited
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: float, causal: bool = True,
+            br: Optional[int] = None, bc: int = 64, scale: Optional[float] = None,
+            out: Optional[torch.Tensor] = None, want_mask: bool = True, want_lse: bool = True,
+            want_stats: bool = True) -> AttnResult:
+    """Skip-softmax prefill. q [B,Hq,Nq,d], k [B,Hkv,Nk,d], v [B,Hkv,Nk,dv] on one GPU."""
+    lib = load_library()
+    _require_device(q, k, v, out)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk, dv = k.shape[1], k.shape[2], v.shape[3]
+    if br is None:
+        br = 64 if q.dtype == torch.float32 else 128
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, Nq, dv), dtype=q.dtype, device=dev)
+    nqt, nkt = -(-Nq // br), -(-Nk // bc)
+    mask = torch.empty((B, Hq, nqt, nkt), dtype=torch.uint8, device=dev) if want_mask else None
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev) if want_lse else None
+    stats = torch.empty((B, Hq, 2), dtype=torch.int64, device=dev) if want_stats else None
+    sh = Shape(B, Hq, Hkv, Nq, Nk, d, dv, _strides3(q), _strides3(k), _strides3(v), _strides3(out))
+    st = lib.blasst_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(mask), _ptr(lse),
+                                 _ptr(stats), ctypes.byref(sh), _dtype_code(q), float(lam),
+                                 float(scale) if scale else 0.0, int(bool(causal)), int(br),
+                                 int(bc), _stream(dev))
+    _check(st)
+    return AttnResult(out, mask, lse, stats)
+
+
+def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], lam: float,
+           bc: int = 64, scale: Optional[float] = None, dv: Optional[int] = None,
+           out: Optional[torch.Tensor] = None, want_mask: bool = True, want_lse: bool = True,
+           want_stats: bool = True) -> AttnResult:
+    """Skip-softmax decode. q [B,Hq,d]; k_cache [B,Hkv,Nk,d]; v_cache [B,Hkv,Nk,dv] or
+    None for a latent cache whose values are k_cache[..., :dv]."""
+    lib = load_library()
+    _require_device(q, k_cache, v_cache, out)
+    B, Hq, d = q.shape
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    if v_cache is not None:
+        dv = v_cache.shape[3]
+    elif dv is None:
+        raise ValueError("dv is required for a latent cache")
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, dv), dtype=q.dtype, device=dev)
+    nkt = -(-Nk // bc)
+    mask = torch.empty((B, Hq, nkt), dtype=torch.uint8, device=dev) if want_mask else None
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if want_lse else None
+    stats = torch.empty((B, Hq, 3), dtype=torch.int64, device=dev) if want_stats else None
+    vs = _strides3(v_cache) if v_cache is not None else (0, 0, 0)
+    sh = Shape(B, Hq, Hkv, 1, Nk, d, dv, _strides3(q), _strides3(k_cache), vs, _strides3(out))
+    st = lib.blasst_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(mask),
+                                _ptr(lse), _ptr(stats), ctypes.byref(sh), _dtype_code(q),
+                                float(lam), float(scale) if scale else 0.0, int(bc), _stream(dev))
+    _check(st)
+    return AttnResult(out, mask, lse, stats)
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+__all__ = ["prefill", "decode", "load_library", "Shape", "BlasstError", "AttnResult",
+           "EXPORTED", "LIB_PATH", "STATUS"]

@@ -1,0 +1,228 @@
+// libblasst C ABI: argument validation and kernel dispatch.
+//
+// Every argument is checked before the first HIP call, so a rejected call
+// launches nothing and leaves every output untouched. No C++ exception crosses
+// the ABI.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/blasst.h"
+#include "common.hpp"
+
+namespace blasst {
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t stream);
+
+__global__ void zero_i64_kernel(int64_t* p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+}  // namespace blasst
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+blasst_status_t fail(blasst_status_t s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+blasst_status_t fail(blasst_status_t s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+blasst_status_t ok() {
+  g_last_error[0] = '\0';
+  return BLASST_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool strides_aligned(const int64_t* s, int n, int elem) {
+  for (int i = 0; i < n; ++i)
+    if (((s[i] * elem) & 15) != 0) return false;
+  return true;
+}
+
+blasst_status_t check_lambda_scale(float lambda, float scale) {
+  if (std::isnan(lambda) || lambda < 0.f || lambda > 1.f)
+    return fail(BLASST_E_LAMBDA, "lambda must lie in [0, 1], got %g", (double)lambda);
+  if (!std::isfinite(scale)) return fail(BLASST_E_ARG, "scale must be finite");
+  return BLASST_OK;
+}
+
+// ln(lambda) / scale, the threshold in raw q.k units (-inf for lambda = 0).
+float raw_threshold(float lambda, float scale) {
+  if (lambda == 0.f) return -INFINITY;
+  return (float)(std::log((double)lambda) / (double)scale);
+}
+
+blasst_status_t hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(BLASST_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+blasst_status_t zero_stats(int64_t* stats, int64_t n, hipStream_t st) {
+  if (!stats || n == 0) return BLASST_OK;
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  hipLaunchKernelGGL(blasst::zero_i64_kernel, dim3(blocks), dim3(256), 0, st, stats, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(BLASST_E_HIP, "stats zero fill: %s", hipGetErrorString(e));
+  return BLASST_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int blasst_version(void) { return BLASST_VERSION; }
+
+const char* blasst_last_error(void) { return g_last_error; }
+
+const char* blasst_status_string(blasst_status_t s) {
+  switch (s) {
+    case BLASST_OK: return "BLASST_OK";
+    case BLASST_E_NULL: return "BLASST_E_NULL: a required pointer is NULL";
+    case BLASST_E_SHAPE: return "BLASST_E_SHAPE: invalid sizes";
+    case BLASST_E_DTYPE: return "BLASST_E_DTYPE: unknown dtype";
+    case BLASST_E_LAMBDA: return "BLASST_E_LAMBDA: lambda outside [0, 1] or NaN";
+    case BLASST_E_ALIGN: return "BLASST_E_ALIGN: pointer or stride not 16-byte aligned";
+    case BLASST_E_UNSUPPORTED: return "BLASST_E_UNSUPPORTED: no kernel for this combination";
+    case BLASST_E_ARG: return "BLASST_E_ARG: invalid scalar argument";
+    case BLASST_E_HIP: return "BLASST_E_HIP: HIP runtime error";
+  }
+  return "BLASST: unknown status";
+}
+
+blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v, void* out,
+                                    uint8_t* mask_out, float* lse_out, int64_t* stats_out,
+                                    const blasst_shape_t* shape, blasst_dtype_t dtype,
+                                    float lambda, float scale, int causal, int br, int bc,
+                                    void* stream) {
+  if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
+  if (!q || !k || !v || !out) return fail(BLASST_E_NULL, "q, k, v and out are required");
+  if (dtype != BLASST_FP32 && dtype != BLASST_BF16)
+    return fail(BLASST_E_DTYPE, "unknown dtype %d", (int)dtype);
+  const blasst_shape_t& s = *shape;
+  if (s.batch < 0 || s.heads_q < 1 || s.heads_kv < 1 || s.len_q < 0 || s.len_kv < 1 ||
+      s.d_qk < 1 || s.d_v < 1)
+    return fail(BLASST_E_SHAPE, "sizes out of range (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d dv=%d)",
+                s.batch, s.heads_q, s.heads_kv, s.len_q, s.len_kv, s.d_qk, s.d_v);
+  if (s.heads_q % s.heads_kv != 0)
+    return fail(BLASST_E_SHAPE, "heads_q (%d) must be a multiple of heads_kv (%d)", s.heads_q,
+                s.heads_kv);
+  if (causal && s.len_q > s.len_kv)
+    return fail(BLASST_E_SHAPE, "causal prefill needs len_q <= len_kv (%d > %d)", s.len_q,
+                s.len_kv);
+  if (br < 1 || bc < 1) return fail(BLASST_E_SHAPE, "tile sizes must be positive");
+  blasst_status_t st = check_lambda_scale(lambda, scale);
+  if (st != BLASST_OK) return st;
+  const int elem = dtype == BLASST_FP32 ? 4 : 2;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+    return fail(BLASST_E_ALIGN, "q, k, v and out must be 16-byte aligned");
+  if (!strides_aligned(s.q_stride, 3, elem) || !strides_aligned(s.k_stride, 3, elem) ||
+      !strides_aligned(s.v_stride, 3, elem) || !strides_aligned(s.o_stride, 3, elem))
+    return fail(BLASST_E_ALIGN, "every stride times the element size must be a multiple of 16");
+  const bool f32 = dtype == BLASST_FP32 && s.d_qk == 64 && s.d_v == 64 && br == 64 && bc == 64;
+  const bool b16 = dtype == BLASST_BF16 && s.d_qk == 128 && s.d_v == 128 && br == 128 && bc == 64;
+  if (!f32 && !b16)
+    return fail(BLASST_E_UNSUPPORTED,
+                "no prefill kernel for dtype=%d d_qk=%d d_v=%d br=%d bc=%d (supported: fp32 "
+                "64/64 64x64, bf16 128/128 128x64)",
+                (int)dtype, s.d_qk, s.d_v, br, bc);
+  const int64_t nqt = ((int64_t)s.len_q + br - 1) / br;
+  const int64_t nkt = ((int64_t)s.len_kv + bc - 1) / bc;
+  if ((int64_t)s.batch * s.heads_q * nqt > 0x7fffffffLL)
+    return fail(BLASST_E_UNSUPPORTED, "grid too large");
+
+  const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)s.d_qk));
+  blasst::PrefillArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out;
+  a.mask = mask_out; a.lse = lse_out; a.stats = stats_out;
+  a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nq = s.len_q; a.Nk = s.len_kv;
+  a.nqt = (int)nqt; a.nkt = (int)nkt; a.causal = causal ? 1 : 0;
+  a.qs0 = s.q_stride[0]; a.qs1 = s.q_stride[1]; a.qs2 = s.q_stride[2];
+  a.ks0 = s.k_stride[0]; a.ks1 = s.k_stride[1]; a.ks2 = s.k_stride[2];
+  a.vs0 = s.v_stride[0]; a.vs1 = s.v_stride[1]; a.vs2 = s.v_stride[2];
+  a.os0 = s.o_stride[0]; a.os1 = s.o_stride[1]; a.os2 = s.o_stride[2];
+  a.scale = sc;
+  a.scale_log2 = sc * blasst::kLog2e;
+  a.thr_raw = raw_threshold(lambda, sc);
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  st = zero_stats(stats_out, (int64_t)s.batch * s.heads_q * 2, hs);
+  if (st != BLASST_OK) return st;
+  if (s.batch == 0 || s.len_q == 0) return ok();
+  const hipError_t e = f32 ? blasst::launch_prefill_f32(a, hs) : blasst::launch_prefill_bf16(a, hs);
+  return hip_status(e, "prefill launch");
+}
+
+blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                   void* out, uint8_t* mask_out, float* lse_out,
+                                   int64_t* stats_out, const blasst_shape_t* shape,
+                                   blasst_dtype_t dtype, float lambda, float scale, int bc,
+                                   void* stream) {
+  if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
+  if (!q || !k_cache || !out) return fail(BLASST_E_NULL, "q, k_cache and out are required");
+  if (dtype != BLASST_FP32 && dtype != BLASST_BF16)
+    return fail(BLASST_E_DTYPE, "unknown dtype %d", (int)dtype);
+  const blasst_shape_t& s = *shape;
+  if (s.batch < 0 || s.heads_q < 1 || s.heads_kv < 1 || s.len_kv < 1 || s.d_qk < 1 || s.d_v < 1)
+    return fail(BLASST_E_SHAPE, "sizes out of range (B=%d Hq=%d Hkv=%d Nk=%d d=%d dv=%d)",
+                s.batch, s.heads_q, s.heads_kv, s.len_kv, s.d_qk, s.d_v);
+  if (s.len_q != 1) return fail(BLASST_E_SHAPE, "decode needs len_q == 1 (got %d)", s.len_q);
+  if (s.heads_q % s.heads_kv != 0)
+    return fail(BLASST_E_SHAPE, "heads_q (%d) must be a multiple of heads_kv (%d)", s.heads_q,
+                s.heads_kv);
+  if (!v_cache && s.d_v >= s.d_qk)
+    return fail(BLASST_E_SHAPE, "a latent cache (v_cache NULL) needs d_v < d_qk");
+  if (bc < 1) return fail(BLASST_E_SHAPE, "tile size must be positive");
+  blasst_status_t st = check_lambda_scale(lambda, scale);
+  if (st != BLASST_OK) return st;
+  const int elem = dtype == BLASST_FP32 ? 4 : 2;
+  if (!aligned16(q) || !aligned16(k_cache) || (v_cache && !aligned16(v_cache)) || !aligned16(out))
+    return fail(BLASST_E_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (!strides_aligned(s.q_stride, 2, elem) || !strides_aligned(s.k_stride, 3, elem) ||
+      (v_cache && !strides_aligned(s.v_stride, 3, elem)) || !strides_aligned(s.o_stride, 2, elem))
+    return fail(BLASST_E_ALIGN, "every stride times the element size must be a multiple of 16");
+  const int G = s.heads_q / s.heads_kv;
+  const bool gqa = dtype == BLASST_BF16 && v_cache && s.d_qk == 128 && s.d_v == 128 && bc == 64 &&
+                   G <= 16;
+  const bool mla = dtype == BLASST_BF16 && !v_cache && s.d_qk == 576 && s.d_v == 512 && bc == 64;
+  if (!gqa && !mla)
+    return fail(BLASST_E_UNSUPPORTED,
+                "no decode kernel for dtype=%d d_qk=%d d_v=%d bc=%d G=%d v_cache=%s (supported: "
+                "bf16 128/128 bc=64 G<=16; bf16 latent 576/512 bc=64)",
+                (int)dtype, s.d_qk, s.d_v, bc, G, v_cache ? "set" : "NULL");
+  if (mla && stats_out && !mask_out)
+    return fail(BLASST_E_NULL, "stats_out for a latent cache needs mask_out (the V-tile count "
+                               "spans several workgroups and is taken from the mask)");
+
+  const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)s.d_qk));
+  blasst::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.out = out;
+  a.mask = mask_out; a.lse = lse_out; a.stats = stats_out;
+  a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nk = s.len_kv; a.G = G;
+  a.nkt = (s.len_kv + bc - 1) / bc;
+  a.qs0 = s.q_stride[0]; a.qs1 = s.q_stride[1];
+  a.ks0 = s.k_stride[0]; a.ks1 = s.k_stride[1]; a.ks2 = s.k_stride[2];
+  a.vs0 = s.v_stride[0]; a.vs1 = s.v_stride[1]; a.vs2 = s.v_stride[2];
+  a.os0 = s.o_stride[0]; a.os1 = s.o_stride[1];
+  a.scale = sc;
+  a.scale_log2 = sc * blasst::kLog2e;
+  a.thr_raw = raw_threshold(lambda, sc);
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (s.batch == 0) return ok();
+  const hipError_t e = gqa ? blasst::launch_decode_gqa(a, hs) : blasst::launch_decode_mla(a, hs);
+  return hip_status(e, "decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,112 @@
+// Device helpers shared by the gfx950 kernels of libblasst.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blasst {
+
+typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8_t;
+typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4_t;
+typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16_t;
+typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4_t;
+typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2_t;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegInf = -__builtin_inff();
+
+// Arguments of every prefill kernel (element strides; last dim contiguous).
+struct PrefillArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* out;
+  uint8_t* mask;   // nullable [B,Hq,nqt,nkt]
+  float* lse;      // nullable [B,Hq,Nq]
+  int64_t* stats;  // nullable [B,Hq,2], zeroed by the launcher
+  int B, Hq, Hkv, Nq, Nk;
+  int nqt, nkt;
+  int causal;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
+  float scale;      // softmax scale applied to q.k
+  float scale_log2; // scale * log2(e)
+  float thr_raw;    // ln(lambda) / scale: the drop threshold in raw q.k units
+};
+
+// Arguments of the decode kernels.
+struct DecodeArgs {
+  const void* q;
+  const void* k;
+  const void* v;  // null for a latent (MLA) cache
+  void* out;
+  uint8_t* mask;   // nullable [B,Hq,nkt]
+  float* lse;      // nullable [B,Hq]
+  int64_t* stats;  // nullable [B,Hq,3]
+  int B, Hq, Hkv, Nk, G;
+  int nkt;
+  int64_t qs0, qs1, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1;
+  float scale, scale_log2, thr_raw;
+};
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> one dword of two bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef __attribute__((__vector_size__(2 * sizeof(__bf16)))) __bf16 bf16x2_t;
+  bf16x2_t r;
+  r[0] = (__bf16)a;
+  r[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Low halves of two dwords -> (lo(a), lo(b)); high halves -> (hi(a), hi(b)).
+__device__ __forceinline__ uint32_t pack_lo16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ f32x16_t mfma32x32x16(const bf16x8_t& a, const bf16x8_t& b,
+                                                 const f32x16_t& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16x16x32(const bf16x8_t& a, const bf16x8_t& b,
+                                                const f32x4_t& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(const u32x4_t& v) {
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int mask) {
+  return __shfl_xor(v, mask, 64);
+}
+
+// Lane l and lane l^32 exchange values (gfx950 v_permlane32_swap). Either
+// order of the returned pair holds {own, partner}; callers only combine them
+// with commutative operations.
+__device__ __forceinline__ float max_with_lane_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_with_lane_xor32(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ u32x4_t load16(const void* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void store16(void* p, const u32x4_t& v) {
+  *reinterpret_cast<u32x4_t*>(p) = v;
+}
+
+__global__ void zero_i64_kernel(int64_t* p, int64_t n);
+
+}  // namespace blasst

@@ -1,0 +1,168 @@
+/*
+ * blasst.h - C ABI of libblasst: BLASST skip-softmax attention on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The operation (sources: the BLASST explainer post "BLASST: Dynamic BLocked
+ * Attention Sparsity via Softmax Thresholding" on the seeallochnaya Telegram
+ * channel, and the digg.com thread "BLASST wins Best Paper at MLSys 2026"):
+ *
+ *   Blocked attention with an online softmax. Keys are cut into tiles of bc
+ *   positions and visited in increasing order (post, paragraph "В чём идея").
+ *   A running per-row maximum of the scaled scores s = scale * q.k is kept and
+ *   earlier partial sums are rescaled when it grows (post, paragraph on the
+ *   online trick of FlashAttention 1). A key tile whose maximum falls far below
+ *   the running maximum is dropped whole: no exp, no row-sum, no P.V, and its
+ *   V rows are never read (post, paragraph beginning "BLASST предлагает"). The
+ *   first tile is always processed (post, first figure). The drop test is one
+ *   scalar threshold on the online softmax statistics (digg thread).
+ *
+ *   Precisely, for a query tile (prefill: br rows; decode: one row) and key
+ *   tile j (visited left to right):
+ *     gap_r = rowmax_r(tile j) - m_r          (m_r = running max; +inf while
+ *                                              m_r is -inf; -inf for a row with
+ *                                              no visible key in the tile)
+ *     g     = max over the tile's valid rows of gap_r
+ *     drop  <=>  j > 0  and  g < ln(lambda)    (strict; ln 0 = -inf)
+ *   Kept tiles get the usual rescale-and-accumulate. For lambda <= 1 a dropped
+ *   tile can never raise the running max, so m_r on entry to tile j equals the
+ *   plain prefix max of the row maxima of tiles 0..j-1.
+ *
+ * Conventions shared by every entry point:
+ *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library
+ *     allocates no memory and keeps no per-call state; calls are reentrant.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the legacy
+ *     default stream). Outputs are valid once the stream has synchronised.
+ *   - All arguments are validated before any HIP call. On any error nothing is
+ *     launched and every output is left untouched. No C++ exception crosses
+ *     the ABI. Launch failures return BLASST_E_HIP; blasst_last_error() then
+ *     holds the HIP error text (thread-local).
+ *   - GQA: query head h reads key/value head h / (heads_q / heads_kv).
+ *   - Causal prefill is bottom-right aligned: query i sits at key position
+ *     len_kv - len_q + i and sees keys 0..len_kv-len_q+i.
+ *   - Tensor pointers must be 16-byte aligned, the last dimension must be
+ *     contiguous, and every stride times the element size must be a multiple
+ *     of 16 bytes (BLASST_E_ALIGN).
+ *   - lambda must satisfy 0 <= lambda <= 1 (BLASST_E_LAMBDA otherwise; NaN is
+ *     rejected). lambda = 0 drops nothing and gives exact softmax attention.
+ *   - scale <= 0 selects 1/sqrt(d_qk); a non-finite scale is BLASST_E_ARG.
+ */
+#ifndef BLASST_H
+#define BLASST_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define BLASST_VERSION 100 /* 1.0.0 */
+
+typedef enum blasst_status {
+  BLASST_OK = 0,
+  BLASST_E_NULL = 1,        /* a required pointer is NULL */
+  BLASST_E_SHAPE = 2,       /* bad sizes: negative, heads_q % heads_kv != 0,
+                               causal with len_q > len_kv, len_q != 1 for decode */
+  BLASST_E_DTYPE = 3,       /* unknown dtype value */
+  BLASST_E_LAMBDA = 4,      /* lambda NaN or outside [0, 1] */
+  BLASST_E_ALIGN = 5,       /* pointer or stride not 16-byte aligned */
+  BLASST_E_UNSUPPORTED = 6, /* valid request with no kernel in this build */
+  BLASST_E_ARG = 7,         /* other bad scalar argument (non-finite scale) */
+  BLASST_E_HIP = 8          /* a HIP runtime call failed */
+} blasst_status_t;
+
+typedef enum blasst_dtype {
+  BLASST_FP32 = 0, /* float32 in, float32 out */
+  BLASST_BF16 = 1  /* bfloat16 in, bfloat16 out (fp32 accumulation) */
+} blasst_dtype_t;
+
+/* Sizes and element strides. Strides are in ELEMENTS for the (batch, head,
+ * position) dimensions; the last (feature) dimension is contiguous. For
+ * decode the query has no position dimension and q_stride[2] / o_stride[2]
+ * are ignored. */
+typedef struct blasst_shape {
+  int32_t batch;    /* B  >= 0 */
+  int32_t heads_q;  /* Hq >= 1 */
+  int32_t heads_kv; /* Hkv >= 1, divides Hq */
+  int32_t len_q;    /* Nq >= 0 (decode: 1) */
+  int32_t len_kv;   /* Nk >= 1 */
+  int32_t d_qk;     /* query/key feature size */
+  int32_t d_v;      /* value/output feature size */
+  int64_t q_stride[3];
+  int64_t k_stride[3];
+  int64_t v_stride[3];
+  int64_t o_stride[3];
+} blasst_shape_t;
+
+/* Mask values written to mask_out. */
+#define BLASST_TILE_DROPPED 0
+#define BLASST_TILE_KEPT 1
+#define BLASST_TILE_NOT_VISITED 2 /* causally empty: no visible (row, key) pair */
+
+/*
+ * Prefill: out = skip-softmax attention of q against k, v.
+ *
+ *   q   [B, Hq,  Nq, d_qk]   (strides q_stride)
+ *   k   [B, Hkv, Nk, d_qk]   (strides k_stride)
+ *   v   [B, Hkv, Nk, d_v]    (strides v_stride)
+ *   out [B, Hq,  Nq, d_v]    (strides o_stride), same dtype as the inputs
+ *   mask_out  nullable, contiguous uint8 [B, Hq, ceil(Nq/br), ceil(Nk/bc)]:
+ *             BLASST_TILE_* per (query tile, key tile)
+ *   lse_out   nullable, contiguous float [B, Hq, Nq]: natural-log
+ *             log-sum-exp of the scaled scores over the KEPT keys
+ *   stats_out nullable, contiguous int64 [B, Hq, 2]: {visited key tiles,
+ *             kept key tiles} summed over the head's query tiles
+ *
+ * Supported (else BLASST_E_UNSUPPORTED):
+ *   BLASST_FP32, d_qk = d_v = 64,  br = 64,  bc = 64
+ *   BLASST_BF16, d_qk = d_v = 128, br = 128, bc = 64
+ */
+blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v, void* out,
+                                    uint8_t* mask_out, float* lse_out, int64_t* stats_out,
+                                    const blasst_shape_t* shape, blasst_dtype_t dtype,
+                                    float lambda, float scale, int causal, int br, int bc,
+                                    void* stream);
+
+/*
+ * Decode: one query token per (batch, query head) against a contiguous KV
+ * cache of len_kv positions (shape->len_q must be 1). Tile 0 is the cache's
+ * first key tile and the running max is global along the whole cache, so the
+ * mask does not depend on how the kernel splits the keys.
+ *
+ *   q       [B, Hq, d_qk]        (strides q_stride[0..1])
+ *   k_cache [B, Hkv, Nk, d_qk]   (strides k_stride)
+ *   v_cache [B, Hkv, Nk, d_v]    (strides v_stride), or NULL: the values are
+ *           the first d_v features of each key (an MLA latent cache); then
+ *           d_v < d_qk and v_stride is ignored
+ *   out     [B, Hq, d_v]         (strides o_stride[0..1])
+ *   mask_out  nullable, contiguous uint8 [B, Hq, ceil(Nk/bc)]
+ *   lse_out   nullable, contiguous float [B, Hq]
+ *   stats_out nullable, contiguous int64 [B, Hq, 3]: {visited key tiles, kept
+ *             key tiles, V tiles read for this head's KV head}. A V tile is
+ *             read when any query head sharing the KV head keeps it.
+ *
+ * Supported (else BLASST_E_UNSUPPORTED), all BLASST_BF16 with bc = 64:
+ *   d_qk = d_v = 128 with a separate v_cache, heads_q / heads_kv <= 16
+ *   d_qk = 576, d_v = 512, v_cache NULL (latent cache), heads_q / heads_kv
+ *   a multiple of 16
+ */
+blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                   void* out, uint8_t* mask_out, float* lse_out,
+                                   int64_t* stats_out, const blasst_shape_t* shape,
+                                   blasst_dtype_t dtype, float lambda, float scale, int bc,
+                                   void* stream);
+
+/* Static text for a status code. */
+const char* blasst_status_string(blasst_status_t status);
+
+/* Detail of the last error on the calling thread ("" if none). */
+const char* blasst_last_error(void);
+
+/* BLASST_VERSION of the loaded library. */
+int blasst_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLASST_H */

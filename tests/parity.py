@@ -1,0 +1,148 @@
+"""Shared parity helpers for the GPU tests: GPU result vs the CPU oracle.
+
+Bar (element by element, on the same seeded inputs):
+  * the kept-tile mask matches exactly, except key tiles whose oracle max-gap
+    lies within BAND of ln(lambda); those flips are logged, and the rows of a
+    query tile touched by a flip are compared with softmax attention restricted
+    to the GPU's own mask (so the output check stays exact in meaning);
+  * bf16 outputs: max-abs <= 1e-2 and mean-abs <= 1e-3; fp32: max-abs <= 1e-5;
+  * lse: 2e-3 (bf16) / 1e-5 (fp32) absolute; stats: exact.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+import torch
+
+import oracle
+from block_sparse_long_skip_amd import synth
+
+BAND = 1e-3
+TOL = {"bf16": dict(max_abs=1e-2, mean_abs=1e-3, lse=2e-3),
+       "fp32": dict(max_abs=1e-5, mean_abs=1e-5, lse=1e-5)}
+
+
+def to_device(x: np.ndarray, w: synth.Workload) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if w.dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to("cuda")
+
+
+def from_device(t: torch.Tensor) -> np.ndarray:
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+@dataclass
+class Tally:
+    """Aggregate of one parity check (errors over every compared element)."""
+    abs_err: list = field(default_factory=list)
+    lse_err: list = field(default_factory=list)
+    tiles: int = 0
+    flips: int = 0
+    band: int = 0
+    notes: list = field(default_factory=list)
+
+    def add(self, err: np.ndarray, lse_err: np.ndarray):
+        self.abs_err.append(np.abs(err).ravel())
+        self.lse_err.append(np.abs(lse_err).ravel())
+
+    def check(self, dtype: str, label: str = ""):
+        tol = TOL[dtype]
+        e = np.concatenate(self.abs_err) if self.abs_err else np.zeros(1)
+        le = np.concatenate(self.lse_err) if self.lse_err else np.zeros(1)
+        msg = (f"{label}: max_abs={e.max():.3e} mean_abs={e.mean():.3e} lse_max={le.max():.3e} "
+               f"tiles={self.tiles} flips={self.flips} near_threshold={self.band}")
+        print(msg, *self.notes[:10], sep="\n  ")
+        assert np.isfinite(e).all(), msg
+        assert e.max() <= tol["max_abs"], msg
+        assert e.mean() <= tol["mean_abs"], msg
+        assert le.max() <= tol["lse"], msg
+        return msg
+
+
+def _thr(lam: float) -> float:
+    return -math.inf if lam == 0 else math.log(lam)
+
+
+def check_mask_row(gpu_row: np.ndarray, orc_row: np.ndarray, gap_row: np.ndarray, lam: float,
+                   tally: Tally, where: str) -> np.ndarray:
+    """Exact mask match outside the near-threshold band. Returns the flip positions."""
+    thr = _thr(lam)
+    visited = orc_row != oracle.MASK_NOT_VISITED
+    assert np.array_equal(gpu_row == oracle.MASK_NOT_VISITED, ~visited), f"{where}: visited set"
+    assert set(np.unique(gpu_row)).issubset({0, 1, 2}), f"{where}: mask values"
+    assert gpu_row[0] == oracle.MASK_KEPT, f"{where}: tile 0 must be kept"
+    near = visited & (np.abs(gap_row - thr) <= BAND) if math.isfinite(thr) else np.zeros_like(visited)
+    tally.band += int(near.sum())
+    flips = visited & (gpu_row != orc_row)
+    bad = flips & ~near
+    assert not bad.any(), (f"{where}: mask differs outside the band at tiles {np.nonzero(bad)[0][:8]}"
+                           f" gaps {gap_row[bad][:8]} thr {thr}")
+    tally.tiles += int(visited.sum())
+    if flips.any():
+        tally.flips += int(flips.sum())
+        tally.notes.append(f"{where}: flipped tiles {np.nonzero(flips)[0].tolist()} "
+                           f"gaps {gap_row[flips].tolist()} thr {thr}")
+    return flips
+
+
+def masked_reference(q_rows, k, v, keep_el, scale):
+    """Softmax over the kept keys only, via the oracle's dense routine (visibility
+    already folded into keep_el)."""
+    return oracle.masked_dense_attention(q_rows, k, v, keep_el, False, scale)
+
+
+def prefill_tile_parity(res, inp, w: synth.Workload, lam: float, b: int, h: int, i: int,
+                        tally: Tally, qf=None, kf=None, vf=None):
+    """Compare one (b, h, query tile i) of a GPU prefill result with the oracle."""
+    G = w.Hq // w.Hkv
+    kvh = h // G
+    r0, r1 = i * w.br, min((i + 1) * w.br, w.Nq)
+    q = qf if qf is not None else synth.to_float(inp.q[b, h, r0:r1], w)
+    k = kf if kf is not None else synth.to_float(inp.k[b, kvh], w)
+    v = vf if vf is not None else synth.to_float(inp.v[b, kvh], w)
+    scale = 1.0 / math.sqrt(w.d)
+    vis = oracle.visible(w.Nq, w.Nk, w.causal, r0, r1 - r0)
+    t = oracle.blasst_rows(q, k, v, lam, w.bc, vis, scale)
+    gpu_mask = res.mask[b, h, i].cpu().numpy()
+    flips = check_mask_row(gpu_mask, t.mask, t.gap, lam, tally, f"b{b} h{h} qtile{i}")
+    ref_out, ref_lse = t.out, t.lse
+    if flips.any():
+        keep_el = oracle.expand_tile_mask(gpu_mask[None, :], r1 - r0, w.bc, r1 - r0, w.Nk) & vis
+        ref_out, ref_lse = masked_reference(q, k, v, keep_el, scale)
+    got = from_device(res.out[b, h, r0:r1])
+    got_lse = res.lse[b, h, r0:r1].cpu().numpy().astype(np.float64)
+    tally.add(got - ref_out, got_lse - ref_lse)
+    return t
+
+
+def decode_row_parity(res, q64, k64, v64, lam: float, bc: int, b: int, hq: int, tally: Tally):
+    """Compare one (b, hq) decode row. q64 [d]; k64 [Nk,d]; v64 [Nk,dv] (float64)."""
+    nk = k64.shape[0]
+    scale = 1.0 / math.sqrt(q64.shape[0])
+    t = oracle.blasst_rows(q64[None], k64, v64, lam, bc, np.ones((1, nk), bool), scale)
+    gpu_mask = res.mask[b, hq].cpu().numpy()
+    flips = check_mask_row(gpu_mask, t.mask, t.gap, lam, tally, f"b{b} h{hq}")
+    ref_out, ref_lse = t.out[0], t.lse[0]
+    if flips.any():
+        keep_el = oracle.expand_tile_mask(gpu_mask[None, :], 1, bc, 1, nk)
+        o, l_ = masked_reference(q64[None], k64, v64, keep_el, scale)
+        ref_out, ref_lse = o[0], l_[0]
+    got = from_device(res.out[b, hq])
+    tally.add(got - ref_out, np.array([float(res.lse[b, hq]) - ref_lse]))
+    return t
+
+
+def sample_qtiles(w: synth.Workload, heads, per_head: int, seed: int):
+    """Query tiles {0, 1, middle, last} plus random ones, for each listed head."""
+    nqt = synth.n_tiles(w.Nq, w.br)
+    rng = np.random.default_rng(seed)
+    out = []
+    for h in heads:
+        base = sorted({0, min(1, nqt - 1), nqt // 2, nqt - 1})
+        extra = rng.choice(nqt, size=min(per_head, nqt), replace=False).tolist()
+        out += [(h, i) for i in sorted(set(base + extra))]
+    return out

@@ -1,0 +1,151 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call (so these
+calls never reach the device). Pointers here are fake, 16-byte-aligned
+addresses: every case below fails validation before anything is launched."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+from block_sparse_long_skip_amd import attention as A
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "blasst.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(A.LIB_PATH),
+                                reason="libblasst.so not built (python -m block_sparse_long_skip_amd.build)")
+
+P = 0x10000  # fake aligned device addresses, never dereferenced
+BF16, FP32 = A.BLASST_BF16, A.BLASST_FP32
+
+
+def _header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(blasst_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    lib = A.load_library()
+    declared = _header_functions()
+    assert set(declared) == set(A.EXPORTED)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert lib.blasst_version() == 100
+
+
+def test_status_strings():
+    lib = A.load_library()
+    for code, name in A.STATUS.items():
+        assert lib.blasst_status_string(code).decode().startswith(name)
+    assert b"unknown" in lib.blasst_status_string(99)
+
+
+def _shape(B=1, Hq=4, Hkv=2, Nq=256, Nk=256, d=128, dv=128, elem=2):
+    def st(n, dd):
+        return (Hq * n * dd, n * dd, dd)
+    return A.Shape(B, Hq, Hkv, Nq, Nk, d, dv, st(Nq, d), (Hkv * Nk * d, Nk * d, d),
+                   (Hkv * Nk * dv, Nk * dv, dv), st(Nq, dv))
+
+
+def _prefill(sh, q=P, k=P, v=P, out=P, dtype=BF16, lam=1e-3, scale=0.0, causal=1, br=128, bc=64,
+             shape_ptr=True):
+    lib = A.load_library()
+    return lib.blasst_attn_prefill(q, k, v, out, None, None, None,
+                                   ctypes.byref(sh) if shape_ptr else None, dtype, lam, scale,
+                                   causal, br, bc, None)
+
+
+def _decode(sh, q=P, k=P, v=P, out=P, mask=None, stats=None, dtype=BF16, lam=1e-3, bc=64):
+    lib = A.load_library()
+    return lib.blasst_attn_decode(q, k, v, out, mask, None, stats, ctypes.byref(sh), dtype, lam,
+                                  0.0, bc, None)
+
+
+def _err():
+    return A.load_library().blasst_last_error().decode()
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_shape", 1), ("null_q", 1), ("null_v", 1), ("bad_dtype", 3), ("heads", 2),
+    ("causal_nq_gt_nk", 2), ("neg_len", 2), ("lam_neg", 4), ("lam_gt1", 4), ("lam_nan", 4),
+    ("scale_inf", 7), ("misaligned_ptr", 5), ("misaligned_stride", 5), ("bad_d", 6),
+    ("bad_tile", 6), ("f32_wrong_d", 6), ("zero_tile", 2),
+])
+def test_prefill_validation(case, expect):
+    sh = _shape()
+    kw = {}
+    if case == "null_shape":
+        kw["shape_ptr"] = False
+    elif case == "null_q":
+        kw["q"] = None
+    elif case == "null_v":
+        kw["v"] = None
+    elif case == "bad_dtype":
+        kw["dtype"] = 5
+    elif case == "heads":
+        sh.heads_q = 3
+    elif case == "causal_nq_gt_nk":
+        sh.len_q, sh.len_kv = 300, 200
+    elif case == "neg_len":
+        sh.len_q = -1
+    elif case == "lam_neg":
+        kw["lam"] = -0.1
+    elif case == "lam_gt1":
+        kw["lam"] = 1.5
+    elif case == "lam_nan":
+        kw["lam"] = math.nan
+    elif case == "scale_inf":
+        kw["scale"] = math.inf
+    elif case == "misaligned_ptr":
+        kw["k"] = P + 8
+    elif case == "misaligned_stride":
+        sh.q_stride[2] = 100  # 200 bytes, not a multiple of 16
+    elif case == "bad_d":
+        sh.d_qk = sh.d_v = 96
+    elif case == "bad_tile":
+        kw["br"] = 64
+    elif case == "f32_wrong_d":
+        kw["dtype"], kw["br"] = FP32, 64
+    elif case == "zero_tile":
+        kw["bc"] = 0
+    assert _prefill(sh, **kw) == expect, _err()
+    assert _err() != ""
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("len_q", 2), ("latent_dv", 2), ("gqa_too_many_heads", 6), ("bad_bc", 6),
+    ("mla_stats_without_mask", 1), ("null_k", 1), ("lam", 4), ("f32", 6),
+])
+def test_decode_validation(case, expect):
+    sh = _shape(Hq=8, Hkv=2, Nq=1, Nk=1000)
+    kw = {}
+    if case == "len_q":
+        sh.len_q = 2
+    elif case == "latent_dv":
+        kw["v"] = None
+        sh.d_v = sh.d_qk
+    elif case == "gqa_too_many_heads":
+        sh.heads_q, sh.heads_kv = 64, 2
+    elif case == "bad_bc":
+        kw["bc"] = 128
+    elif case == "mla_stats_without_mask":
+        sh = _shape(Hq=32, Hkv=1, Nq=1, Nk=1000, d=576, dv=512)
+        kw["v"], kw["stats"] = None, P
+    elif case == "null_k":
+        kw["k"] = None
+    elif case == "lam":
+        kw["lam"] = 2.0
+    elif case == "f32":
+        kw["dtype"] = FP32
+    assert _decode(sh, **kw) == expect, _err()
+
+
+def test_binding_has_no_cpu_fallback():
+    """The Python binding refuses CPU tensors instead of computing anything."""
+    import torch
+    q = torch.zeros(1, 1, 64, 64)
+    with pytest.raises(Exception):
+        A.prefill(q, q, q, 0.0)

@@ -1,0 +1,251 @@
+"""GPU parity: every HIP kernel against the CPU oracle, through the C ABI.
+
+Small cases span several tiles with ragged tails and run the whole oracle;
+the full-size workloads (Llama-3.1-8B-shaped prefill at N=32768, Qwen2.5-7B-
+shaped prefill at N=131072, batch-32 GQA decode over 65536 keys, batch-16 MLA
+decode over 32768 latent keys) run the kernel in the launch configuration the
+benchmark times and compare sampled query tiles / rows with the oracle.
+The supplementary gain (planted boosts scaled by g) makes dropped tiles appear;
+at gain 1 the workloads as specified drop nothing.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_sparse_long_skip_amd import attention as A
+from block_sparse_long_skip_amd import synth
+from parity import Tally, decode_row_parity, from_device, prefill_tile_parity, sample_qtiles, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    A.load_library()
+    yield
+    torch.cuda.synchronize()
+
+
+def _prefill(inp, w, lam, **kw):
+    q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    r = A.prefill(q, k, v, lam, causal=w.causal, br=w.br, bc=w.bc, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _decode(inp, w, lam):
+    q, k = to_device(inp.q, w), to_device(inp.k, w)
+    v = to_device(inp.v, w) if inp.v is not None else None
+    r = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv)
+    torch.cuda.synchronize()
+    return r
+
+
+def _check_prefill_full(w, lam, label):
+    inp = synth.make_inputs(w)
+    res = _prefill(inp, w, lam)
+    tally = Tally()
+    nqt = synth.n_tiles(w.Nq, w.br)
+    stats_mask = res.mask.cpu().numpy()
+    for b in range(w.B):
+        for h in range(w.Hq):
+            for i in range(nqt):
+                prefill_tile_parity(res, inp, w, lam, b, h, i, tally)
+    st = res.stats.cpu().numpy()
+    assert np.array_equal(st[..., 0], (stats_mask != 2).sum(axis=(2, 3)))
+    assert np.array_equal(st[..., 1], (stats_mask == 1).sum(axis=(2, 3)))
+    tally.check(w.dtype, label)
+    return res
+
+
+# ----------------------------------------------------------------------------- prefill fp32
+
+@pytest.mark.parametrize("gain", [1.0, 6.0])
+@pytest.mark.parametrize("lam", [0.0, 1e-3, 1e-2])
+def test_prefill_fp32_n1024(lam, gain):
+    w = synth.WORKLOADS[1].with_gain(gain)
+    res = _check_prefill_full(w, lam, f"fp32 n1024 lam={lam} g={gain}")
+    if gain == 6.0 and lam > 0:
+        assert res.skip_fraction > 0.0
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=2, Hq=4, Hkv=2, Nq=200, Nk=200, causal=True),
+    dict(B=1, Hq=2, Hkv=1, Nq=70, Nk=333, causal=True),    # bottom-right alignment
+    dict(B=1, Hq=3, Hkv=3, Nq=129, Nk=65, causal=False),
+    dict(B=1, Hq=1, Hkv=1, Nq=1, Nk=130, causal=True),
+])
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-2, 6.0), (1.0, 6.0)])
+def test_prefill_fp32_ragged(shape, lam, gain):
+    w = synth.small_workload("prefill", d=64, dtype="fp32", br=64, bc=64, gain=gain, seed=21,
+                             **shape)
+    _check_prefill_full(w, lam, f"fp32 {shape} lam={lam}")
+
+
+# ----------------------------------------------------------------------------- prefill bf16
+
+@pytest.mark.parametrize("shape", [
+    dict(B=1, Hq=2, Hkv=1, Nq=300, Nk=300, causal=True),
+    dict(B=2, Hq=4, Hkv=2, Nq=130, Nk=333, causal=True),
+    dict(B=1, Hq=2, Hkv=2, Nq=200, Nk=129, causal=False),
+    dict(B=1, Hq=1, Hkv=1, Nq=128, Nk=128, causal=True),
+    dict(B=1, Hq=1, Hkv=1, Nq=5, Nk=64, causal=True),
+    dict(B=1, Hq=1, Hkv=1, Nq=1, Nk=1, causal=True),
+])
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 1.0), (1e-2, 6.0), (1.0, 6.0)])
+def test_prefill_bf16_small(shape, lam, gain):
+    w = synth.small_workload("prefill", d=128, dtype="bf16", br=128, bc=64, gain=gain, seed=33,
+                             window=32, **shape)
+    _check_prefill_full(w, lam, f"bf16 {shape} lam={lam} g={gain}")
+
+
+def _prefill_sampled(cfg, lam, gain, heads, per_head, seed):
+    w = synth.WORKLOADS[cfg].with_gain(gain)
+    inp = synth.make_inputs(w)
+    res = _prefill(inp, w, lam)
+    tally = Tally()
+    kv_cache = {}
+    for (h, i) in sample_qtiles(w, heads, per_head, seed):
+        kvh = h // w.G
+        if kvh not in kv_cache:
+            kv_cache = {kvh: (synth.to_float(inp.k[0, kvh], w), synth.to_float(inp.v[0, kvh], w))}
+        kf, vf = kv_cache[kvh]
+        prefill_tile_parity(res, inp, w, lam, 0, h, i, tally, kf=kf, vf=vf)
+    # whole-call invariants on the GPU mask
+    m = res.mask.cpu().numpy()
+    nqt, nkt = m.shape[2], m.shape[3]
+    assert (m[..., 0] == 1).all()
+    last_vis = (np.minimum((np.arange(nqt) + 1) * w.br, w.Nq) - 1 + w.Nk - w.Nq) // w.bc
+    assert ((m == 2) == (np.arange(nkt)[None, :] > last_vis[:, None])[None, None]).all()
+    st = res.stats.cpu().numpy()
+    assert np.array_equal(st[..., 1], (m == 1).sum(axis=(2, 3)))
+    tally.check(w.dtype, f"workload {cfg} lam={lam} g={gain}")
+    return res
+
+
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-4, 1.0), (1e-3, 1.0), (1e-2, 1.0),
+                                      (1e-3, 6.0), (1e-2, 6.0)])
+def test_prefill_llama8b_n32768(lam, gain):
+    res = _prefill_sampled(2, lam, gain, heads=[0, 5, 31], per_head=3, seed=2)
+    if gain == 1.0:
+        assert res.skip_fraction == 0.0  # the as-specified planting is too weak to drop tiles
+    else:
+        assert res.skip_fraction > 0.05
+
+
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 1.0), (1e-3, 8.0)])
+def test_prefill_qwen7b_n131072(lam, gain):
+    _prefill_sampled(4, lam, gain, heads=[0, 27], per_head=1, seed=4)
+
+
+# ----------------------------------------------------------------------------- decode
+
+def _check_decode(w, lam, pairs=None):
+    inp = synth.make_inputs(w)
+    res = _decode(inp, w, lam)
+    tally = Tally()
+    if pairs is None:
+        pairs = [(b, kvh) for b in range(w.B) for kvh in range(w.Hkv)]
+    for (b, kvh) in pairs:
+        kf = synth.to_float(inp.k[b, kvh], w)
+        vf = kf[:, :w.dv] if inp.v is None else synth.to_float(inp.v[b, kvh], w)
+        for hq in range(kvh * w.G, (kvh + 1) * w.G):
+            decode_row_parity(res, synth.to_float(inp.q[b, hq], w), kf, vf, lam, w.bc, b, hq, tally)
+    m = res.mask.cpu().numpy()
+    st = res.stats.cpu().numpy()
+    nkt = m.shape[2]
+    assert (st[..., 0] == nkt).all() and (m[..., 0] == 1).all()
+    assert np.array_equal(st[..., 1], (m == 1).sum(axis=2))
+    for b in range(w.B):
+        for kvh in range(w.Hkv):
+            grp = m[b, kvh * w.G:(kvh + 1) * w.G]
+            assert (st[b, kvh * w.G:(kvh + 1) * w.G, 2] == (grp == 1).any(axis=0).sum()).all()
+    tally.check(w.dtype, f"decode {w.name} lam={lam} g={w.gain}")
+    return res
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=2, Hq=8, Hkv=2, Nk=1000),
+    dict(B=1, Hq=16, Hkv=1, Nk=777),
+    dict(B=3, Hq=3, Hkv=3, Nk=64),
+    dict(B=1, Hq=5, Hkv=1, Nk=1),
+    dict(B=2, Hq=4, Hkv=1, Nk=4100),
+])
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 6.0), (1e-2, 6.0), (1.0, 6.0)])
+def test_decode_gqa_small(shape, lam, gain):
+    w = synth.small_workload("decode", d=128, dtype="bf16", bc=64, gain=gain, seed=44,
+                             window=64, **shape)
+    _check_decode(w, lam)
+
+
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 1.0), (1e-2, 6.0)])
+def test_decode_gqa_b32_n65536(lam, gain):
+    w = synth.WORKLOADS[3].with_gain(gain)
+    res = _check_decode(w, lam, pairs=[(0, 0), (7, 3), (31, 7)])
+    if gain > 1:
+        assert res.skip_fraction > 0.3
+
+
+@pytest.mark.parametrize("shape", [
+    dict(B=2, Hq=32, Hkv=1, Nk=1000),
+    dict(B=1, Hq=20, Hkv=2, Nk=300),
+    dict(B=1, Hq=16, Hkv=1, Nk=64),
+])
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-2, 6.0)])
+def test_decode_mla_small(shape, lam, gain):
+    w = synth.small_workload("decode_mla", d=576, dv=512, dtype="bf16", bc=64, gain=gain,
+                             seed=55, window=64, **shape)
+    _check_decode(w, lam)
+
+
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-2, 1.0), (1e-2, 6.0)])
+def test_decode_mla_b16_n32768(lam, gain):
+    w = synth.WORKLOADS[5].with_gain(gain)
+    _check_decode(w, lam, pairs=[(0, 0), (15, 0)])
+
+
+# ----------------------------------------------------------------------------- behaviour
+
+def test_rejected_call_leaves_outputs_untouched():
+    w = synth.small_workload("prefill", Nq=200, Nk=200, seed=3)
+    inp = synth.make_inputs(w)
+    q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    out = torch.full((1, w.Hq, 200, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(A.BlasstError) as e:
+        A.prefill(q, k, v, 1.5, out=out)
+    assert e.value.status == 4
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()
+
+
+def test_bitwise_repeatable_and_lambda_nesting():
+    w = synth.WORKLOADS[2].scaled(Nq=4096, Nk=4096).with_gain(6.0)
+    inp = synth.make_inputs(w)
+    prev = None
+    for lam in (0.0, 1e-4, 1e-3, 1e-2, 0.1, 1.0):
+        r1 = _prefill(inp, w, lam)
+        r2 = _prefill(inp, w, lam)
+        assert torch.equal(r1.out.view(torch.int16), r2.out.view(torch.int16))
+        assert torch.equal(r1.mask, r2.mask)
+        kept = (r1.mask == 1).cpu().numpy()
+        if prev is not None:
+            assert not (kept & ~prev).any()
+        prev = kept
+
+
+def test_strided_layout_matches_contiguous():
+    """[B, N, H, d] storage (heads interleaved) gives the same bits as [B, H, N, d]."""
+    w = synth.small_workload("prefill", B=2, Hq=4, Hkv=2, Nq=257, Nk=257, seed=9, gain=6.0)
+    inp = synth.make_inputs(w)
+    q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    ref = A.prefill(q, k, v, 1e-2)
+    qs, ks, vs = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    assert qs.stride(2) == w.Hq * w.d
+    got = A.prefill(qs, ks, vs, 1e-2)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.out.view(torch.int16), got.out.view(torch.int16))
+    assert torch.equal(ref.mask, got.mask)

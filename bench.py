@@ -1,0 +1,344 @@
+#!/usr/bin/env python3
+"""Benchmark: BLASST skip-softmax attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one skip-softmax prefill call (the whole hot path: QK^T on MFMA, the
+per-tile drop vote, V loads and P.V for kept tiles, the output, lse, the tile
+mask and the statistics) over the Llama-3.1-8B-shaped layer: causal, B=1,
+32 query / 8 KV heads, N=32768, d=128, bf16, 128x64 tiles, seeded synthetic
+inputs already resident in HBM. The line printed on stdout carries:
+
+  value        dense-equivalent TFLOP/s = 2 (d + dv) B Hq P / t, where P is the
+               number of visible (query, key) pairs (causal: N(N+1)/2); the
+               same numerator is used for every lambda
+  roofline     the prefill kernel against the bf16 MFMA peak (2.5 PFLOP/s):
+               algorithmic FLOPs per launch (2 Br Bc d per visited tile for
+               QK^T plus 2 Br Bc dv per kept tile for P.V) / mean launch time
+               from HIP events on the launch stream; HBM traffic per launch
+               from rocprofv3 counters when the committed counter summary
+               matches the current kernel source
+  lambda_sweep every lambda of the workload, at gain 1 (the workload as
+               specified, nothing is dropped) and at the supplementary gain 6
+               (planted boosts scaled so tiles are dropped): TFLOP/s, skip
+               fraction and speed-up over lambda = 0
+  decode       the batch-32 GQA decode over 65536 keys and the batch-16 MLA
+               decode over 32768 latent keys: GB/s of the bytes actually read
+               (K always, V only for tiles some head keeps) against 8 TB/s
+  cpu_baseline the CPU oracle timed on a bounded sample of query tiles of the
+               same workload (a reported baseline, not a target)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+PREFILL_SOURCES = ["block_sparse_long_skip_amd/csrc/prefill_bf16.hip",
+                   "block_sparse_long_skip_amd/csrc/common.hpp"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(paths) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--lam", type=float, default=1e-3, help="headline lambda")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
+    ap.add_argument("--only", choices=["prefill", "decode_gqa", "decode_mla", "copy"],
+                    help="launch only this kernel --steps times (for rocprofv3 counter passes)")
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------- helpers
+
+def to_device(x, w):
+    import numpy as np
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x))
+    if w.dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to("cuda")
+
+
+def time_calls(fn, steps, warmup):
+    """Run fn() warmup times, then time `steps` calls with HIP events on the current
+    stream. Returns (mean ms per call from events, wall ms per step, last result)."""
+    import torch
+    res = None
+    for _ in range(warmup):
+        res = fn()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        starts[s].record()
+        res = fn()
+        ends[s].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ev = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
+    return ev, wall, res
+
+
+def prefill_algorithmic_flops(w, stats):
+    st = stats.double()
+    visited = st[..., 0].sum().item()
+    kept = st[..., 1].sum().item()
+    return 2.0 * w.br * w.bc * (w.d * visited + w.dv * kept), visited, kept
+
+
+def read_traffic(kind: str, sha: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source."""
+    path = os.path.join(PROFILE_DIR, f"{kind}.pmc.json")
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha") != sha:
+        return None, "kernel changed since the counters were taken"
+    return d.get("hbm_bytes_per_launch"), path
+
+
+# --------------------------------------------------------------------------- legs
+
+def bench_prefill(args):
+    import torch
+    from block_sparse_long_skip_amd import attention as A
+    from block_sparse_long_skip_amd import synth
+
+    w = synth.WORKLOADS[2]
+    log(f"[bench] generating {w.name} (gain 1)")
+    inp = synth.make_inputs(w)
+    q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    dense = synth.dense_equivalent_flops(w)
+
+    def call(lam):
+        return A.prefill(q, k, v, lam, causal=True, br=w.br, bc=w.bc)
+
+    log(f"[bench] timing prefill lambda={args.lam} steps={args.steps} warmup={args.warmup}")
+    ev_ms, wall_ms, res = time_calls(lambda: call(args.lam), args.steps, args.warmup)
+    alg, visited, kept = prefill_algorithmic_flops(w, res.stats)
+    value = dense / (ev_ms * 1e-3) / 1e12
+    achieved = alg / (ev_ms * 1e-3) / 1e12
+    sha = source_sha(PREFILL_SOURCES)
+    traffic, tnote = read_traffic("prefill_bf16_llama8b_n32768", sha)
+    out = dict(value=value, ms_per_step=ev_ms, wall_ms_per_step=wall_ms,
+               skip_fraction=1.0 - kept / visited, visited_tiles=int(visited), kept_tiles=int(kept),
+               roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
+                             unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
+                             traffic=traffic, traffic_note=tnote,
+                             algorithmic_flops_per_launch=alg,
+                             kernel="prefill_bf16_kernel", kernel_source_sha=sha))
+    sweep = []
+    if not args.no_sweep:
+        for gain in (1.0, 6.0):
+            if gain != 1.0:
+                log(f"[bench] generating gain {gain}")
+                gi = synth.make_inputs(w.with_gain(gain))
+                q2, k2, v2 = (to_device(x, w) for x in (gi.q, gi.k, gi.v))
+            else:
+                q2, k2, v2 = q, k, v
+            base = None
+            for lam in w.lambdas:
+                ms, _, r = time_calls(lambda: A.prefill(q2, k2, v2, lam, causal=True, br=w.br, bc=w.bc),
+                                      max(3, args.steps // 2), 1)
+                base = ms if lam == 0.0 else base
+                sweep.append(dict(gain=gain, lam=lam, tflops=round(dense / (ms * 1e-3) / 1e12, 2),
+                                  ms=round(ms, 4), skip_fraction=round(r.skip_fraction, 4),
+                                  speedup_vs_lam0=round(base / ms, 3) if base else None))
+                log(f"[bench]   gain {gain} lam {lam}: {ms:.3f} ms, skip {r.skip_fraction:.3f}")
+            del q2, k2, v2
+    out["sweep"] = sweep
+    return out, w
+
+
+def bench_decode(args):
+    import torch
+    from block_sparse_long_skip_amd import attention as A
+    from block_sparse_long_skip_amd import synth
+
+    results = {}
+    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB, evicts L2 and MALL
+    for cid, kind in ((3, "decode_gqa_b32_n65536"), (5, "decode_mla_b16_n32768")):
+        w = synth.WORKLOADS[cid]
+        rows = []
+        for gain in (1.0, 6.0):
+            log(f"[bench] generating {w.name} gain {gain}")
+            inp = synth.make_inputs(w.with_gain(gain))
+            q, k = to_device(inp.q, w), to_device(inp.k, w)
+            v = to_device(inp.v, w) if inp.v is not None else None
+            del inp
+            for lam in w.lambdas:
+                times = []
+                res = None
+                for it in range(max(3, args.steps // 2) + 1):
+                    flush.fill_(it)
+                    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    s.record()
+                    res = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv)
+                    e.record()
+                    torch.cuda.synchronize()
+                    if it > 0:
+                        times.append(s.elapsed_time(e))
+                ms = sum(times) / len(times)
+                st = res.stats.double()
+                G = w.G
+                vtiles = st[:, ::G, 2].sum().item()  # per (batch, KV head)
+                kbytes = w.B * w.Hkv * w.Nk * w.d * 2
+                vbytes = vtiles * w.bc * w.dv * 2 if v is not None else 0
+                qo = w.B * w.Hq * (w.d + w.dv) * 2
+                byt = kbytes + vbytes + qo
+                gbs = byt / (ms * 1e-3) / 1e9
+                rows.append(dict(gain=gain, lam=lam, ms=round(ms, 4), gbs=round(gbs, 1),
+                                 frac_hbm=round(gbs / PEAK_HBM_GBS, 4),
+                                 bytes_read=int(byt), skip_fraction=round(res.skip_fraction, 4),
+                                 v_tiles_read_fraction=(round(vtiles / (w.B * w.Hkv * res.mask.shape[2]), 4)
+                                                        if v is not None else None)))
+                log(f"[bench]   {kind} gain {gain} lam {lam}: {ms:.3f} ms {gbs:.0f} GB/s "
+                    f"skip {res.skip_fraction:.3f}")
+            del q, k, v
+            torch.cuda.empty_cache()
+        results[kind] = rows
+    del flush
+    return results
+
+
+def cpu_baseline(args, w):
+    """The oracle, as it stands, on a time-bounded sample of query tiles (head 0,
+    tiles drawn at random), at the headline lambda; dense-equivalent TFLOP/s."""
+    import numpy as np
+    import oracle
+    from block_sparse_long_skip_amd import synth
+
+    threads = None
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((d.get("num_threads") or 0) for d in threadpool_info()) or None
+    except Exception:  # noqa: BLE001
+        pass
+    cores = threads or len(os.sched_getaffinity(0))
+    u = synth.unit_direction(w)
+    kf = synth.to_float(synth.k_slice(w, 0, 0, u), w)
+    vf = synth.to_float(synth.v_slice(w, 0, 0), w)
+    qh = synth.to_float(synth.q_slice(w, 0, 0, u), w)
+    nqt = synth.n_tiles(w.Nq, w.br)
+    order = np.random.default_rng(12345).permutation(nqt)
+    flops, done, t0 = 0.0, [], time.perf_counter()
+    scale = 1.0 / math.sqrt(w.d)
+    for i in order:
+        r0, r1 = i * w.br, min((i + 1) * w.br, w.Nq)
+        vis = oracle.visible(w.Nq, w.Nk, True, r0, r1 - r0)
+        oracle.blasst_rows(qh[r0:r1], kf, vf, args.lam, w.bc, vis, scale)
+        flops += 2.0 * (w.d + w.dv) * float(vis.sum())
+        done.append(int(i))
+        if time.perf_counter() - t0 > args.cpu_seconds:
+            break
+    dt = time.perf_counter() - t0
+    return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
+                sample=f"{len(done)} of {nqt} query tiles of head 0 (random order, seed 12345), "
+                       f"lambda={args.lam}, float64 NumPy, {dt:.1f} s",
+                seconds=round(dt, 2))
+
+
+def only(args):
+    """Launch a single kernel `steps` times (used under rocprofv3 counter passes)."""
+    import torch
+    from block_sparse_long_skip_amd import attention as A
+    from block_sparse_long_skip_amd import synth
+    if args.only == "copy":
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] copied {n} bytes x {args.steps}")
+        return
+    cid = {"prefill": 2, "decode_gqa": 3, "decode_mla": 5}[args.only]
+    w = synth.WORKLOADS[cid]
+    inp = synth.make_inputs(w)
+    q, k = to_device(inp.q, w), to_device(inp.k, w)
+    v = to_device(inp.v, w) if inp.v is not None else None
+    for _ in range(args.steps):
+        if w.kind == "prefill":
+            A.prefill(q, k, v, args.lam, causal=True, br=w.br, bc=w.bc, want_stats=False)
+        else:
+            A.decode(q, k, v, args.lam, bc=w.bc, dv=w.dv, want_stats=False)
+    torch.cuda.synchronize()
+    log(f"[bench] launched {args.only} x {args.steps}")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the kernels run on a single MI355X; sharding is described in the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from block_sparse_long_skip_amd import attention as A
+    A.load_library()
+    if args.only:
+        only(args)
+        return
+    t_start = time.perf_counter()
+    pre, w = bench_prefill(args)
+    decode = None if args.no_decode else bench_decode(args)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(args, w)
+    line = {
+        "metric": "dense-equiv attention TFLOP/s + decode KV GB/s vs roofline, skip fraction per λ",
+        "value": round(pre["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(pre["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded planted sinks/needles/recent window, gain 1)",
+        "config": {"workload": "prefill_llama8b_n32768: causal B=1 Hq=32 Hkv=8 N=32768 d=128 "
+                               "bf16 128x64 tiles", "lambda": args.lam, "gain": 1.0,
+                   "out_dtype": "bf16", "skip_fraction": round(pre["skip_fraction"], 4)},
+        "roofline": pre["roofline"],
+        "cpu_baseline": cpu,
+        "lambda_sweep": pre["sweep"],
+        "decode": decode,
+        "wall_s": round(time.perf_counter() - t_start, 1),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -67,12 +67,13 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, i64p, u8p, fp = ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p
     lib.blasst_attn_prefill.restype = ctypes.c_int
     lib.blasst_attn_prefill.argtypes = [vp, vp, vp, vp, u8p, fp, i64p, ctypes.POINTER(Shape),
-                                        ctypes.c_int, ctypes.c_float, ctypes.c_float,
-                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, vp]
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                        ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        vp]
     lib.blasst_attn_decode.restype = ctypes.c_int
     lib.blasst_attn_decode.argtypes = [vp, vp, vp, vp, u8p, fp, i64p, ctypes.POINTER(Shape),
-                                       ctypes.c_int, ctypes.c_float, ctypes.c_float,
-                                       ctypes.c_int, vp]
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                       ctypes.c_float, ctypes.c_int, vp]
     lib.blasst_status_string.restype = ctypes.c_char_p
     lib.blasst_status_string.argtypes = [ctypes.c_int]
     lib.blasst_last_error.restype = ctypes.c_char_p
@@ -89,12 +90,12 @@ def _check(status: int) -> None:
         raise BlasstError(status, detail)
 
 
-def _dtype_code(t: torch.Tensor) -> int:
-    if t.dtype == torch.float32:
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.float32:
         return BLASST_FP32
-    if t.dtype == torch.bfloat16:
+    if dt == torch.bfloat16:
         return BLASST_BF16
-    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+    raise TypeError(f"unsupported dtype {dt} (float32 or bfloat16)")
 
 
 def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
@@ -135,9 +136,12 @@ class AttnResult:
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: float, causal: bool = True,
             br: Optional[int] = None, bc: int = 64, scale: Optional[float] = None,
-            out: Optional[torch.Tensor] = None, want_mask: bool = True, want_lse: bool = True,
+            out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+            want_mask: bool = True, want_lse: bool = True,
             want_stats: bool = True) -> AttnResult:
-    """Skip-softmax prefill. q [B,Hq,Nq,d], k [B,Hkv,Nk,d], v [B,Hkv,Nk,dv] on one GPU."""
+    """Skip-softmax prefill. q [B,Hq,Nq,d], k [B,Hkv,Nk,d], v [B,Hkv,Nk,dv] on one GPU.
+
+    out_dtype defaults to the input dtype; bfloat16 inputs may ask for float32."""
     lib = load_library()
     _require_device(q, k, v, out)
     B, Hq, Nq, d = q.shape
@@ -146,14 +150,15 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: float, causa
         br = 64 if q.dtype == torch.float32 else 128
     dev = q.device
     if out is None:
-        out = torch.empty((B, Hq, Nq, dv), dtype=q.dtype, device=dev)
+        out = torch.empty((B, Hq, Nq, dv), dtype=out_dtype or q.dtype, device=dev)
     nqt, nkt = -(-Nq // br), -(-Nk // bc)
     mask = torch.empty((B, Hq, nqt, nkt), dtype=torch.uint8, device=dev) if want_mask else None
     lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev) if want_lse else None
     stats = torch.empty((B, Hq, 2), dtype=torch.int64, device=dev) if want_stats else None
     sh = Shape(B, Hq, Hkv, Nq, Nk, d, dv, _strides3(q), _strides3(k), _strides3(v), _strides3(out))
     st = lib.blasst_attn_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(mask), _ptr(lse),
-                                 _ptr(stats), ctypes.byref(sh), _dtype_code(q), float(lam),
+                                 _ptr(stats), ctypes.byref(sh), _dtype_code(q.dtype),
+                                 _dtype_code(out.dtype), float(lam),
                                  float(scale) if scale else 0.0, int(bool(causal)), int(br),
                                  int(bc), _stream(dev))
     _check(st)
@@ -162,7 +167,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: float, causa
 
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], lam: float,
            bc: int = 64, scale: Optional[float] = None, dv: Optional[int] = None,
-           out: Optional[torch.Tensor] = None, want_mask: bool = True, want_lse: bool = True,
+           out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
+           want_mask: bool = True, want_lse: bool = True,
            want_stats: bool = True) -> AttnResult:
     """Skip-softmax decode. q [B,Hq,d]; k_cache [B,Hkv,Nk,d]; v_cache [B,Hkv,Nk,dv] or
     None for a latent cache whose values are k_cache[..., :dv]."""
@@ -176,7 +182,7 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tenso
         raise ValueError("dv is required for a latent cache")
     dev = q.device
     if out is None:
-        out = torch.empty((B, Hq, dv), dtype=q.dtype, device=dev)
+        out = torch.empty((B, Hq, dv), dtype=out_dtype or q.dtype, device=dev)
     nkt = -(-Nk // bc)
     mask = torch.empty((B, Hq, nkt), dtype=torch.uint8, device=dev) if want_mask else None
     lse = torch.empty((B, Hq), dtype=torch.float32, device=dev) if want_lse else None
@@ -184,8 +190,8 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tenso
     vs = _strides3(v_cache) if v_cache is not None else (0, 0, 0)
     sh = Shape(B, Hq, Hkv, 1, Nk, d, dv, _strides3(q), _strides3(k_cache), vs, _strides3(out))
     st = lib.blasst_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(mask),
-                                _ptr(lse), _ptr(stats), ctypes.byref(sh), _dtype_code(q),
-                                float(lam), float(scale) if scale else 0.0, int(bc), _stream(dev))
+                                _ptr(lse), _ptr(stats), ctypes.byref(sh), _dtype_code(q.dtype),
+                                _dtype_code(out.dtype), float(lam), float(scale) if scale else 0.0, int(bc), _stream(dev))
     _check(st)
     return AttnResult(out, mask, lse, stats)
 

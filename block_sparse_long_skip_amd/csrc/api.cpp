@@ -51,6 +51,15 @@ bool strides_aligned(const int64_t* s, int n, int elem) {
   return true;
 }
 
+blasst_status_t check_dtypes(blasst_dtype_t in, blasst_dtype_t out) {
+  if (in != BLASST_FP32 && in != BLASST_BF16) return fail(BLASST_E_DTYPE, "unknown dtype %d", (int)in);
+  if (out != BLASST_FP32 && out != BLASST_BF16)
+    return fail(BLASST_E_DTYPE, "unknown out_dtype %d", (int)out);
+  if (in == BLASST_FP32 && out != BLASST_FP32)
+    return fail(BLASST_E_DTYPE, "float32 inputs write float32 outputs");
+  return BLASST_OK;
+}
+
 blasst_status_t check_lambda_scale(float lambda, float scale) {
   if (std::isnan(lambda) || lambda < 0.f || lambda > 1.f)
     return fail(BLASST_E_LAMBDA, "lambda must lie in [0, 1], got %g", (double)lambda);
@@ -104,12 +113,13 @@ const char* blasst_status_string(blasst_status_t s) {
 blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v, void* out,
                                     uint8_t* mask_out, float* lse_out, int64_t* stats_out,
                                     const blasst_shape_t* shape, blasst_dtype_t dtype,
-                                    float lambda, float scale, int causal, int br, int bc,
-                                    void* stream) {
+                                    blasst_dtype_t out_dtype, float lambda, float scale,
+                                    int causal, int br, int bc, void* stream) {
+  blasst_status_t st0;
   if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
   if (!q || !k || !v || !out) return fail(BLASST_E_NULL, "q, k, v and out are required");
-  if (dtype != BLASST_FP32 && dtype != BLASST_BF16)
-    return fail(BLASST_E_DTYPE, "unknown dtype %d", (int)dtype);
+  st0 = check_dtypes(dtype, out_dtype);
+  if (st0 != BLASST_OK) return st0;
   const blasst_shape_t& s = *shape;
   if (s.batch < 0 || s.heads_q < 1 || s.heads_kv < 1 || s.len_q < 0 || s.len_kv < 1 ||
       s.d_qk < 1 || s.d_v < 1)
@@ -125,10 +135,11 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
   blasst_status_t st = check_lambda_scale(lambda, scale);
   if (st != BLASST_OK) return st;
   const int elem = dtype == BLASST_FP32 ? 4 : 2;
+  const int oelem = out_dtype == BLASST_FP32 ? 4 : 2;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
     return fail(BLASST_E_ALIGN, "q, k, v and out must be 16-byte aligned");
   if (!strides_aligned(s.q_stride, 3, elem) || !strides_aligned(s.k_stride, 3, elem) ||
-      !strides_aligned(s.v_stride, 3, elem) || !strides_aligned(s.o_stride, 3, elem))
+      !strides_aligned(s.v_stride, 3, elem) || !strides_aligned(s.o_stride, 3, oelem))
     return fail(BLASST_E_ALIGN, "every stride times the element size must be a multiple of 16");
   const bool f32 = dtype == BLASST_FP32 && s.d_qk == 64 && s.d_v == 64 && br == 64 && bc == 64;
   const bool b16 = dtype == BLASST_BF16 && s.d_qk == 128 && s.d_v == 128 && br == 128 && bc == 64;
@@ -148,6 +159,7 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
   a.mask = mask_out; a.lse = lse_out; a.stats = stats_out;
   a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nq = s.len_q; a.Nk = s.len_kv;
   a.nqt = (int)nqt; a.nkt = (int)nkt; a.causal = causal ? 1 : 0;
+  a.out_f32 = out_dtype == BLASST_FP32 ? 1 : 0;
   a.qs0 = s.q_stride[0]; a.qs1 = s.q_stride[1]; a.qs2 = s.q_stride[2];
   a.ks0 = s.k_stride[0]; a.ks1 = s.k_stride[1]; a.ks2 = s.k_stride[2];
   a.vs0 = s.v_stride[0]; a.vs1 = s.v_stride[1]; a.vs2 = s.v_stride[2];
@@ -167,12 +179,13 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
 blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                                    void* out, uint8_t* mask_out, float* lse_out,
                                    int64_t* stats_out, const blasst_shape_t* shape,
-                                   blasst_dtype_t dtype, float lambda, float scale, int bc,
-                                   void* stream) {
+                                   blasst_dtype_t dtype, blasst_dtype_t out_dtype, float lambda,
+                                   float scale, int bc, void* stream) {
+  blasst_status_t st0;
   if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
   if (!q || !k_cache || !out) return fail(BLASST_E_NULL, "q, k_cache and out are required");
-  if (dtype != BLASST_FP32 && dtype != BLASST_BF16)
-    return fail(BLASST_E_DTYPE, "unknown dtype %d", (int)dtype);
+  st0 = check_dtypes(dtype, out_dtype);
+  if (st0 != BLASST_OK) return st0;
   const blasst_shape_t& s = *shape;
   if (s.batch < 0 || s.heads_q < 1 || s.heads_kv < 1 || s.len_kv < 1 || s.d_qk < 1 || s.d_v < 1)
     return fail(BLASST_E_SHAPE, "sizes out of range (B=%d Hq=%d Hkv=%d Nk=%d d=%d dv=%d)",
@@ -187,10 +200,11 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
   blasst_status_t st = check_lambda_scale(lambda, scale);
   if (st != BLASST_OK) return st;
   const int elem = dtype == BLASST_FP32 ? 4 : 2;
+  const int oelem = out_dtype == BLASST_FP32 ? 4 : 2;
   if (!aligned16(q) || !aligned16(k_cache) || (v_cache && !aligned16(v_cache)) || !aligned16(out))
     return fail(BLASST_E_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
   if (!strides_aligned(s.q_stride, 2, elem) || !strides_aligned(s.k_stride, 3, elem) ||
-      (v_cache && !strides_aligned(s.v_stride, 3, elem)) || !strides_aligned(s.o_stride, 2, elem))
+      (v_cache && !strides_aligned(s.v_stride, 3, elem)) || !strides_aligned(s.o_stride, 2, oelem))
     return fail(BLASST_E_ALIGN, "every stride times the element size must be a multiple of 16");
   const int G = s.heads_q / s.heads_kv;
   const bool gqa = dtype == BLASST_BF16 && v_cache && s.d_qk == 128 && s.d_v == 128 && bc == 64 &&
@@ -211,6 +225,7 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
   a.mask = mask_out; a.lse = lse_out; a.stats = stats_out;
   a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nk = s.len_kv; a.G = G;
   a.nkt = (s.len_kv + bc - 1) / bc;
+  a.out_f32 = out_dtype == BLASST_FP32 ? 1 : 0;
   a.qs0 = s.q_stride[0]; a.qs1 = s.q_stride[1];
   a.ks0 = s.k_stride[0]; a.ks1 = s.k_stride[1]; a.ks2 = s.k_stride[2];
   a.vs0 = s.v_stride[0]; a.vs1 = s.v_stride[1]; a.vs2 = s.v_stride[2];

@@ -28,6 +28,7 @@ struct PrefillArgs {
   int B, Hq, Hkv, Nq, Nk;
   int nqt, nkt;
   int causal;
+  int out_f32;  // 1: out is float32, 0: out is bfloat16
   int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2;
   float scale;      // softmax scale applied to q.k
   float scale_log2; // scale * log2(e)
@@ -45,6 +46,7 @@ struct DecodeArgs {
   int64_t* stats;  // nullable [B,Hq,3]
   int B, Hq, Hkv, Nk, G;
   int nkt;
+  int out_f32;  // 1: out is float32, 0: out is bfloat16
   int64_t qs0, qs1, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1;
   float scale, scale_log2, thr_raw;
 };
@@ -98,6 +100,21 @@ __device__ __forceinline__ float max_with_lane_xor32(float v) {
 __device__ __forceinline__ float sum_with_lane_xor32(float v) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Store 4 consecutive output features as bf16 (8 bytes) or float32 (16 bytes).
+__device__ __forceinline__ void store_out4(void* out, int64_t elem_off, bool f32, float a,
+                                           float b, float c, float d) {
+  if (f32) {
+    *reinterpret_cast<f32x4_t*>(static_cast<float*>(out) + elem_off) = (f32x4_t){a, b, c, d};
+  } else {
+    *reinterpret_cast<u32x2_t*>(static_cast<uint16_t*>(out) + elem_off) =
+        (u32x2_t){pack_bf16x2(a, b), pack_bf16x2(c, d)};
+  }
+}
+__device__ __forceinline__ void store_out1(void* out, int64_t elem_off, bool f32, float a) {
+  if (f32) static_cast<float*>(out)[elem_off] = a;
+  else static_cast<uint16_t*>(out)[elem_off] = (uint16_t)(pack_bf16x2(a, 0.f) & 0xffffu);
 }
 
 __device__ __forceinline__ u32x4_t load16(const void* p) {

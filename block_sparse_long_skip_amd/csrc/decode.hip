@@ -240,8 +240,7 @@ __global__ void __launch_bounds__(GNT) decode_gqa_kernel(DecodeArgs a) {
       acc += px[dv * 16 + hn] * wgt;
     }
     const int hh = kvh * G + hn;
-    uint16_t* op = (uint16_t*)a.out + b * a.os0 + (int64_t)hh * a.os1;
-    op[dv] = (uint16_t)(pack_bf16x2(acc / L, 0.f) & 0xffffu);
+    store_out1(a.out, b * a.os0 + (int64_t)hh * a.os1 + dv, a.out_f32, acc / L);
     if (dv == 0) {
       if (a.lse) a.lse[(int64_t)b * a.Hq + hh] = M * a.scale + logf(L);
       if (a.stats) {
@@ -373,14 +372,11 @@ __global__ void __launch_bounds__(MNT) decode_mla_kernel(DecodeArgs a, int ngrou
   const float L = lred[0][n] + lred[1][n] + lred[2][n] + lred[3][n];
   if (hvalid) {
     const float inv = 1.f / L;
-    uint16_t* op = (uint16_t*)a.out + b * a.os0 + (int64_t)hq * a.os1;
+    const int64_t ob = b * a.os0 + (int64_t)hq * a.os1;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const int dv = 128 * w + 16 * db + 4 * g;
-      u32x2_t v = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv),
-                   pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
-      *(u32x2_t*)(op + dv) = v;
-    }
+    for (int db = 0; db < 8; ++db)
+      store_out4(a.out, ob + 128 * w + 16 * db + 4 * g, a.out_f32, o[db][0] * inv, o[db][1] * inv,
+                 o[db][2] * inv, o[db][3] * inv);
     if (w == 0 && g == 0) {
       if (a.lse) a.lse[(int64_t)b * a.Hq + hq] = m * a.scale + logf(L);
       if (a.stats) {

@@ -210,16 +210,13 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const float lt = sum_with_lane_xor32(l);
   if (valid) {
     const float inv = 1.f / lt;
-    uint16_t* op = (uint16_t*)a.out + b * a.os0 + hq * a.os1 + (int64_t)row * a.os2;
+    const int64_t ob = b * a.os0 + hq * a.os1 + (int64_t)row * a.os2;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int dv = 32 * db + 8 * qd + 4 * h;
-        u32x2_t v = {pack_bf16x2(o[db][4 * qd] * inv, o[db][4 * qd + 1] * inv),
-                     pack_bf16x2(o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv)};
-        *(u32x2_t*)(op + dv) = v;
-      }
+      for (int qd = 0; qd < 4; ++qd)
+        store_out4(a.out, ob + 32 * db + 8 * qd + 4 * h, a.out_f32, o[db][4 * qd] * inv,
+                   o[db][4 * qd + 1] * inv, o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv);
     if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + row] = m * a.scale + logf(lt);
   }
   if (a.stats && t == 0) {

@@ -13,6 +13,10 @@
 // tile vote is a plain wave ballot; the four waves share the running max (the
 // row max of a tile is combined through LDS) and keep separate partial row
 // sums and outputs, summed once at the end.
+//
+// Scores q.k are accumulated in fp64 and the running max is kept in fp64, so
+// large logits (strongly peaked attention) lose no precision before the
+// exponent; P.V and the row sums accumulate in fp32.
 #include "common.hpp"
 
 namespace blasst {
@@ -26,7 +30,7 @@ constexpr int NT = 256;
 
 __global__ void __launch_bounds__(NT) prefill_f32_kernel(PrefillArgs a) {
   __shared__ float smem[2 * BC * D];
-  __shared__ float red[4][BR];
+  __shared__ double red[4][BR];
   float (*Ks)[D] = reinterpret_cast<float (*)[D]>(smem);
   float (*Vs)[D] = reinterpret_cast<float (*)[D]>(smem + BC * D);
 
@@ -67,7 +71,8 @@ __global__ void __launch_bounds__(NT) prefill_f32_kernel(PrefillArgs a) {
   float o[D];
 #pragma unroll
   for (int x = 0; x < D; ++x) o[x] = 0.f;
-  float m = kNegInf, l = 0.f;
+  double m = -__builtin_inf();
+  float l = 0.f;
   int kept = 0;
   uint8_t* mrow = a.mask ? a.mask + ((int64_t)bh * a.nqt + i) * a.nkt : nullptr;
 
@@ -85,34 +90,34 @@ __global__ void __launch_bounds__(NT) prefill_f32_kernel(PrefillArgs a) {
     }
     __syncthreads();
 
-    float s[16];
-    float pm = kNegInf;
+    double s[16];
+    double pm = -__builtin_inf();
 #pragma unroll
     for (int cc = 0; cc < 16; ++cc) {
       const int col = c0 + 16 * w + cc;
-      float acc = 0.f;
+      double acc = 0.0;
 #pragma unroll
       for (int x = 0; x < D; x += 4) {
         f32x4_t kv = *(const f32x4_t*)&Ks[16 * w + cc][x];
-        acc = fmaf(q[x], kv[0], acc);
-        acc = fmaf(q[x + 1], kv[1], acc);
-        acc = fmaf(q[x + 2], kv[2], acc);
-        acc = fmaf(q[x + 3], kv[3], acc);
+        acc = fma((double)q[x], (double)kv[0], acc);
+        acc = fma((double)q[x + 1], (double)kv[1], acc);
+        acc = fma((double)q[x + 2], (double)kv[2], acc);
+        acc = fma((double)q[x + 3], (double)kv[3], acc);
       }
       const bool vis = col < a.Nk && (!a.causal || col <= qpos);
-      s[cc] = vis ? acc : kNegInf;
-      pm = fmaxf(pm, s[cc]);
+      s[cc] = vis ? acc : -__builtin_inf();
+      pm = fmax(pm, s[cc]);
     }
     red[w][lane] = pm;
     __syncthreads();
-    const float mt = fmaxf(fmaxf(red[0][lane], red[1][lane]), fmaxf(red[2][lane], red[3][lane]));
+    const double mt = fmax(fmax(red[0][lane], red[1][lane]), fmax(red[2][lane], red[3][lane]));
 
     // tile vote: drop only if every valid row's gap is below the threshold
-    float gap;
-    if (mt == kNegInf) gap = kNegInf;
-    else if (m == kNegInf) gap = __builtin_inff();
+    double gap;
+    if (mt == -__builtin_inf()) gap = -__builtin_inf();
+    else if (m == -__builtin_inf()) gap = __builtin_inf();
     else gap = mt - m;
-    const bool lane_keep = valid && !(gap < a.thr_raw);
+    const bool lane_keep = valid && !(gap < (double)a.thr_raw);
     const bool keep = (j == 0) || __any(lane_keep);
 
     if (keep) {
@@ -126,15 +131,16 @@ __global__ void __launch_bounds__(NT) prefill_f32_kernel(PrefillArgs a) {
         *(f32x4_t*)&Vs[vr][vc] = v;
       }
       __syncthreads();
-      const float m_new = fmaxf(m, mt);
-      const float mc = (m_new == kNegInf) ? 0.f : m_new * a.scale_log2;
-      const float alpha = fast_exp2(m * a.scale_log2 - mc);
+      const double m_new = fmax(m, mt);
+      const double mref = (m_new == -__builtin_inf()) ? 0.0 : m_new;
+      const double sl2 = (double)a.scale * 1.4426950408889634;
+      const float alpha = fast_exp2((float)((m - mref) * sl2));
       l *= alpha;
 #pragma unroll
       for (int x = 0; x < D; ++x) o[x] *= alpha;
 #pragma unroll
       for (int cc = 0; cc < 16; ++cc) {
-        const float p = fast_exp2(fmaf(s[cc], a.scale_log2, -mc));
+        const float p = fast_exp2((float)((s[cc] - mref) * sl2));
         l += p;
 #pragma unroll
         for (int x = 0; x < D; x += 4) {
@@ -156,8 +162,9 @@ __global__ void __launch_bounds__(NT) prefill_f32_kernel(PrefillArgs a) {
 
   // combine the four waves' partial sums (same running max in every wave)
   __syncthreads();
+  __syncthreads();
   float* acc = smem;  // reuse LDS: [64 rows][D + 1], padded against bank conflicts
-  red[w][lane] = l;
+  red[w][lane] = (double)l;
   for (int src = 1; src < 4; ++src) {
     if (w == src) {
 #pragma unroll
@@ -171,16 +178,16 @@ __global__ void __launch_bounds__(NT) prefill_f32_kernel(PrefillArgs a) {
     __syncthreads();
   }
   if (w == 0) {
-    const float lt = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
+    const double lt = red[0][lane] + red[1][lane] + red[2][lane] + red[3][lane];
     if (valid) {
-      const float inv = 1.f / lt;
+      const float inv = (float)(1.0 / lt);
       float* op = (float*)a.out + b * a.os0 + hq * a.os1 + (int64_t)row * a.os2;
 #pragma unroll
       for (int x = 0; x < D; x += 4) {
         f32x4_t v = {o[x] * inv, o[x + 1] * inv, o[x + 2] * inv, o[x + 3] * inv};
         *(f32x4_t*)(op + x) = v;
       }
-      if (a.lse) a.lse[(int64_t)bh * a.Nq + row] = m * a.scale + logf(lt);
+      if (a.lse) a.lse[(int64_t)bh * a.Nq + row] = (float)(m * (double)a.scale + log(lt));
     }
     if (a.stats && lane == 0) {
       atomicAdd((unsigned long long*)&a.stats[2 * bh], (unsigned long long)J);

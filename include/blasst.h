@@ -63,7 +63,7 @@ typedef enum blasst_status {
   BLASST_E_NULL = 1,        /* a required pointer is NULL */
   BLASST_E_SHAPE = 2,       /* bad sizes: negative, heads_q % heads_kv != 0,
                                causal with len_q > len_kv, len_q != 1 for decode */
-  BLASST_E_DTYPE = 3,       /* unknown dtype value */
+  BLASST_E_DTYPE = 3,       /* unknown dtype or unsupported input/output pair */
   BLASST_E_LAMBDA = 4,      /* lambda NaN or outside [0, 1] */
   BLASST_E_ALIGN = 5,       /* pointer or stride not 16-byte aligned */
   BLASST_E_UNSUPPORTED = 6, /* valid request with no kernel in this build */
@@ -72,9 +72,14 @@ typedef enum blasst_status {
 } blasst_status_t;
 
 typedef enum blasst_dtype {
-  BLASST_FP32 = 0, /* float32 in, float32 out */
-  BLASST_BF16 = 1  /* bfloat16 in, bfloat16 out (fp32 accumulation) */
+  BLASST_FP32 = 0, /* float32 */
+  BLASST_BF16 = 1  /* bfloat16 */
 } blasst_dtype_t;
+
+/* Input and output element types. `dtype` is the type of q, k and v;
+ * `out_dtype` the type of out. bfloat16 inputs accumulate in fp32 and may
+ * write bfloat16 (rounded to nearest even) or float32 outputs; float32 inputs
+ * write float32 outputs. Anything else is BLASST_E_DTYPE. */
 
 /* Sizes and element strides. Strides are in ELEMENTS for the (batch, head,
  * position) dimensions; the last (feature) dimension is contiguous. For
@@ -105,7 +110,7 @@ typedef struct blasst_shape {
  *   q   [B, Hq,  Nq, d_qk]   (strides q_stride)
  *   k   [B, Hkv, Nk, d_qk]   (strides k_stride)
  *   v   [B, Hkv, Nk, d_v]    (strides v_stride)
- *   out [B, Hq,  Nq, d_v]    (strides o_stride), same dtype as the inputs
+ *   out [B, Hq,  Nq, d_v]    (strides o_stride), element type out_dtype
  *   mask_out  nullable, contiguous uint8 [B, Hq, ceil(Nq/br), ceil(Nk/bc)]:
  *             BLASST_TILE_* per (query tile, key tile)
  *   lse_out   nullable, contiguous float [B, Hq, Nq]: natural-log
@@ -120,8 +125,8 @@ typedef struct blasst_shape {
 blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v, void* out,
                                     uint8_t* mask_out, float* lse_out, int64_t* stats_out,
                                     const blasst_shape_t* shape, blasst_dtype_t dtype,
-                                    float lambda, float scale, int causal, int br, int bc,
-                                    void* stream);
+                                    blasst_dtype_t out_dtype, float lambda, float scale,
+                                    int causal, int br, int bc, void* stream);
 
 /*
  * Decode: one query token per (batch, query head) against a contiguous KV
@@ -134,23 +139,25 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
  *   v_cache [B, Hkv, Nk, d_v]    (strides v_stride), or NULL: the values are
  *           the first d_v features of each key (an MLA latent cache); then
  *           d_v < d_qk and v_stride is ignored
- *   out     [B, Hq, d_v]         (strides o_stride[0..1])
+ *   out     [B, Hq, d_v]         (strides o_stride[0..1]), element type out_dtype
  *   mask_out  nullable, contiguous uint8 [B, Hq, ceil(Nk/bc)]
  *   lse_out   nullable, contiguous float [B, Hq]
  *   stats_out nullable, contiguous int64 [B, Hq, 3]: {visited key tiles, kept
  *             key tiles, V tiles read for this head's KV head}. A V tile is
  *             read when any query head sharing the KV head keeps it.
  *
- * Supported (else BLASST_E_UNSUPPORTED), all BLASST_BF16 with bc = 64:
+ * Supported (else BLASST_E_UNSUPPORTED), all BLASST_BF16 inputs with bc = 64:
  *   d_qk = d_v = 128 with a separate v_cache, heads_q / heads_kv <= 16
- *   d_qk = 576, d_v = 512, v_cache NULL (latent cache), heads_q / heads_kv
- *   a multiple of 16
+ *   d_qk = 576, d_v = 512, v_cache NULL (latent cache), any heads_q / heads_kv
+ *   (the query heads of a KV head are processed in groups of 16). For a
+ *   latent cache, stats_out requires mask_out: the V-tile count spans the
+ *   workgroups of several head groups and is taken from the mask.
  */
 blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                                    void* out, uint8_t* mask_out, float* lse_out,
                                    int64_t* stats_out, const blasst_shape_t* shape,
-                                   blasst_dtype_t dtype, float lambda, float scale, int bc,
-                                   void* stream);
+                                   blasst_dtype_t dtype, blasst_dtype_t out_dtype, float lambda,
+                                   float scale, int bc, void* stream);
 
 /* Static text for a status code. */
 const char* blasst_status_string(blasst_status_t status);

@@ -5,8 +5,12 @@ Bar (element by element, on the same seeded inputs):
     lies within BAND of ln(lambda); those flips are logged, and the rows of a
     query tile touched by a flip are compared with softmax attention restricted
     to the GPU's own mask (so the output check stays exact in meaning);
-  * bf16 outputs: max-abs <= 1e-2 and mean-abs <= 1e-3; fp32: max-abs <= 1e-5;
-  * lse: 2e-3 (bf16) / 1e-5 (fp32) absolute; stats: exact.
+  * arithmetic of bf16-input kernels (float32 outputs): max-abs <= 1e-2 and
+    mean-abs <= 1e-3; fp32 kernels: max-abs <= 1e-5;
+  * bf16 outputs: the same bound plus the round-to-nearest-even storage bound
+    of the output itself, 2^-9 |ref| per element (added to the max bound
+    elementwise and to the mean bound as its mean);
+  * lse: 2e-3 (bf16 inputs) / 1e-5 (fp32) absolute; stats: exact.
 """
 from __future__ import annotations
 
@@ -22,6 +26,7 @@ from block_sparse_long_skip_amd import synth
 BAND = 1e-3
 TOL = {"bf16": dict(max_abs=1e-2, mean_abs=1e-3, lse=2e-3),
        "fp32": dict(max_abs=1e-5, mean_abs=1e-5, lse=1e-5)}
+BF16_STORE = 2.0 ** -9  # relative bound of bf16 round-to-nearest-even
 
 
 def to_device(x: np.ndarray, w: synth.Workload) -> torch.Tensor:
@@ -39,26 +44,33 @@ def from_device(t: torch.Tensor) -> np.ndarray:
 class Tally:
     """Aggregate of one parity check (errors over every compared element)."""
     abs_err: list = field(default_factory=list)
+    ref_abs: list = field(default_factory=list)
     lse_err: list = field(default_factory=list)
     tiles: int = 0
     flips: int = 0
     band: int = 0
     notes: list = field(default_factory=list)
 
-    def add(self, err: np.ndarray, lse_err: np.ndarray):
+    def add(self, err: np.ndarray, lse_err: np.ndarray, ref: np.ndarray):
         self.abs_err.append(np.abs(err).ravel())
+        self.ref_abs.append(np.abs(ref).ravel())
         self.lse_err.append(np.abs(lse_err).ravel())
 
-    def check(self, dtype: str, label: str = ""):
+    def check(self, dtype: str, label: str = "", out_bf16: bool = False):
+        """dtype: input type ("bf16"/"fp32"); out_bf16: outputs were stored as bf16."""
         tol = TOL[dtype]
         e = np.concatenate(self.abs_err) if self.abs_err else np.zeros(1)
+        r = np.concatenate(self.ref_abs) if self.ref_abs else np.zeros(1)
         le = np.concatenate(self.lse_err) if self.lse_err else np.zeros(1)
+        store = BF16_STORE * r if out_bf16 else np.zeros_like(r)
         msg = (f"{label}: max_abs={e.max():.3e} mean_abs={e.mean():.3e} lse_max={le.max():.3e} "
-               f"tiles={self.tiles} flips={self.flips} near_threshold={self.band}")
+               f"excess_over_bound={np.max(e - tol['max_abs'] - store):.3e} "
+               f"tiles={self.tiles} flips={self.flips} near_threshold={self.band} "
+               f"out={'bf16' if out_bf16 else 'fp32'}")
         print(msg, *self.notes[:10], sep="\n  ")
         assert np.isfinite(e).all(), msg
-        assert e.max() <= tol["max_abs"], msg
-        assert e.mean() <= tol["mean_abs"], msg
+        assert (e <= tol["max_abs"] + store).all(), msg
+        assert e.mean() <= tol["mean_abs"] + store.mean(), msg
         assert le.max() <= tol["lse"], msg
         return msg
 
@@ -115,7 +127,7 @@ def prefill_tile_parity(res, inp, w: synth.Workload, lam: float, b: int, h: int,
         ref_out, ref_lse = masked_reference(q, k, v, keep_el, scale)
     got = from_device(res.out[b, h, r0:r1])
     got_lse = res.lse[b, h, r0:r1].cpu().numpy().astype(np.float64)
-    tally.add(got - ref_out, got_lse - ref_lse)
+    tally.add(got - ref_out, got_lse - ref_lse, ref_out)
     return t
 
 
@@ -132,7 +144,7 @@ def decode_row_parity(res, q64, k64, v64, lam: float, bc: int, b: int, hq: int, 
         o, l_ = masked_reference(q64[None], k64, v64, keep_el, scale)
         ref_out, ref_lse = o[0], l_[0]
     got = from_device(res.out[b, hq])
-    tally.add(got - ref_out, np.array([float(res.lse[b, hq]) - ref_lse]))
+    tally.add(got - ref_out, np.array([float(res.lse[b, hq]) - ref_lse]), ref_out)
     return t
 
 

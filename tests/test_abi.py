@@ -51,17 +51,19 @@ def _shape(B=1, Hq=4, Hkv=2, Nq=256, Nk=256, d=128, dv=128, elem=2):
 
 
 def _prefill(sh, q=P, k=P, v=P, out=P, dtype=BF16, lam=1e-3, scale=0.0, causal=1, br=128, bc=64,
-             shape_ptr=True):
+             shape_ptr=True, out_dtype=None):
     lib = A.load_library()
     return lib.blasst_attn_prefill(q, k, v, out, None, None, None,
-                                   ctypes.byref(sh) if shape_ptr else None, dtype, lam, scale,
+                                   ctypes.byref(sh) if shape_ptr else None, dtype,
+                                   dtype if out_dtype is None else out_dtype, lam, scale,
                                    causal, br, bc, None)
 
 
-def _decode(sh, q=P, k=P, v=P, out=P, mask=None, stats=None, dtype=BF16, lam=1e-3, bc=64):
+def _decode(sh, q=P, k=P, v=P, out=P, mask=None, stats=None, dtype=BF16, lam=1e-3, bc=64,
+            out_dtype=None):
     lib = A.load_library()
-    return lib.blasst_attn_decode(q, k, v, out, mask, None, stats, ctypes.byref(sh), dtype, lam,
-                                  0.0, bc, None)
+    return lib.blasst_attn_decode(q, k, v, out, mask, None, stats, ctypes.byref(sh), dtype,
+                                  dtype if out_dtype is None else out_dtype, lam, 0.0, bc, None)
 
 
 def _err():
@@ -72,7 +74,8 @@ def _err():
     ("null_shape", 1), ("null_q", 1), ("null_v", 1), ("bad_dtype", 3), ("heads", 2),
     ("causal_nq_gt_nk", 2), ("neg_len", 2), ("lam_neg", 4), ("lam_gt1", 4), ("lam_nan", 4),
     ("scale_inf", 7), ("misaligned_ptr", 5), ("misaligned_stride", 5), ("bad_d", 6),
-    ("bad_tile", 6), ("f32_wrong_d", 6), ("zero_tile", 2),
+    ("bad_tile", 6), ("f32_wrong_d", 6), ("zero_tile", 2), ("f32_in_bf16_out", 3),
+    ("bad_out_dtype", 3),
 ])
 def test_prefill_validation(case, expect):
     sh = _shape()
@@ -111,6 +114,11 @@ def test_prefill_validation(case, expect):
         kw["dtype"], kw["br"] = FP32, 64
     elif case == "zero_tile":
         kw["bc"] = 0
+    elif case == "f32_in_bf16_out":
+        kw["dtype"], kw["out_dtype"], kw["br"] = FP32, BF16, 64
+        sh.d_qk = sh.d_v = 64
+    elif case == "bad_out_dtype":
+        kw["out_dtype"] = 9
     assert _prefill(sh, **kw) == expect, _err()
     assert _err() != ""
 

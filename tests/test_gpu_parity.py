@@ -30,24 +30,28 @@ def _gpu():
     torch.cuda.synchronize()
 
 
-def _prefill(inp, w, lam, **kw):
+OUT = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def _prefill(inp, w, lam, out="native", **kw):
     q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
-    r = A.prefill(q, k, v, lam, causal=w.causal, br=w.br, bc=w.bc, **kw)
+    od = OUT.get(out)
+    r = A.prefill(q, k, v, lam, causal=w.causal, br=w.br, bc=w.bc, out_dtype=od, **kw)
     torch.cuda.synchronize()
     return r
 
 
-def _decode(inp, w, lam):
+def _decode(inp, w, lam, out="native"):
     q, k = to_device(inp.q, w), to_device(inp.k, w)
     v = to_device(inp.v, w) if inp.v is not None else None
-    r = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv)
+    r = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv, out_dtype=OUT.get(out))
     torch.cuda.synchronize()
     return r
 
 
-def _check_prefill_full(w, lam, label):
+def _check_prefill_full(w, lam, label, out="native"):
     inp = synth.make_inputs(w)
-    res = _prefill(inp, w, lam)
+    res = _prefill(inp, w, lam, out)
     tally = Tally()
     nqt = synth.n_tiles(w.Nq, w.br)
     stats_mask = res.mask.cpu().numpy()
@@ -58,7 +62,7 @@ def _check_prefill_full(w, lam, label):
     st = res.stats.cpu().numpy()
     assert np.array_equal(st[..., 0], (stats_mask != 2).sum(axis=(2, 3)))
     assert np.array_equal(st[..., 1], (stats_mask == 1).sum(axis=(2, 3)))
-    tally.check(w.dtype, label)
+    tally.check(w.dtype, label, out_bf16=res.out.dtype == torch.bfloat16)
     return res
 
 
@@ -97,16 +101,17 @@ def test_prefill_fp32_ragged(shape, lam, gain):
     dict(B=1, Hq=1, Hkv=1, Nq=1, Nk=1, causal=True),
 ])
 @pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 1.0), (1e-2, 6.0), (1.0, 6.0)])
-def test_prefill_bf16_small(shape, lam, gain):
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_prefill_bf16_small(shape, lam, gain, out):
     w = synth.small_workload("prefill", d=128, dtype="bf16", br=128, bc=64, gain=gain, seed=33,
                              window=32, **shape)
-    _check_prefill_full(w, lam, f"bf16 {shape} lam={lam} g={gain}")
+    _check_prefill_full(w, lam, f"bf16 {shape} lam={lam} g={gain}", out)
 
 
-def _prefill_sampled(cfg, lam, gain, heads, per_head, seed):
+def _prefill_sampled(cfg, lam, gain, heads, per_head, seed, out="bf16"):
     w = synth.WORKLOADS[cfg].with_gain(gain)
     inp = synth.make_inputs(w)
-    res = _prefill(inp, w, lam)
+    res = _prefill(inp, w, lam, out)
     tally = Tally()
     kv_cache = {}
     for (h, i) in sample_qtiles(w, heads, per_head, seed):
@@ -123,14 +128,16 @@ def _prefill_sampled(cfg, lam, gain, heads, per_head, seed):
     assert ((m == 2) == (np.arange(nkt)[None, :] > last_vis[:, None])[None, None]).all()
     st = res.stats.cpu().numpy()
     assert np.array_equal(st[..., 1], (m == 1).sum(axis=(2, 3)))
-    tally.check(w.dtype, f"workload {cfg} lam={lam} g={gain}")
+    tally.check(w.dtype, f"workload {cfg} lam={lam} g={gain}", out_bf16=out == "bf16")
     return res
 
 
-@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-4, 1.0), (1e-3, 1.0), (1e-2, 1.0),
-                                      (1e-3, 6.0), (1e-2, 6.0)])
-def test_prefill_llama8b_n32768(lam, gain):
-    res = _prefill_sampled(2, lam, gain, heads=[0, 5, 31], per_head=3, seed=2)
+@pytest.mark.parametrize("lam,gain,out", [(0.0, 1.0, "bf16"), (1e-4, 1.0, "bf16"),
+                                          (1e-3, 1.0, "bf16"), (1e-2, 1.0, "bf16"),
+                                          (1e-3, 6.0, "bf16"), (1e-2, 6.0, "bf16"),
+                                          (1e-2, 6.0, "fp32")])
+def test_prefill_llama8b_n32768(lam, gain, out):
+    res = _prefill_sampled(2, lam, gain, heads=[0, 5, 31], per_head=3, seed=2, out=out)
     if gain == 1.0:
         assert res.skip_fraction == 0.0  # the as-specified planting is too weak to drop tiles
     else:
@@ -144,9 +151,9 @@ def test_prefill_qwen7b_n131072(lam, gain):
 
 # ----------------------------------------------------------------------------- decode
 
-def _check_decode(w, lam, pairs=None):
+def _check_decode(w, lam, pairs=None, out="bf16"):
     inp = synth.make_inputs(w)
-    res = _decode(inp, w, lam)
+    res = _decode(inp, w, lam, out)
     tally = Tally()
     if pairs is None:
         pairs = [(b, kvh) for b in range(w.B) for kvh in range(w.Hkv)]
@@ -164,7 +171,7 @@ def _check_decode(w, lam, pairs=None):
         for kvh in range(w.Hkv):
             grp = m[b, kvh * w.G:(kvh + 1) * w.G]
             assert (st[b, kvh * w.G:(kvh + 1) * w.G, 2] == (grp == 1).any(axis=0).sum()).all()
-    tally.check(w.dtype, f"decode {w.name} lam={lam} g={w.gain}")
+    tally.check(w.dtype, f"decode {w.name} lam={lam} g={w.gain}", out_bf16=out == "bf16")
     return res
 
 
@@ -176,16 +183,18 @@ def _check_decode(w, lam, pairs=None):
     dict(B=2, Hq=4, Hkv=1, Nk=4100),
 ])
 @pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 6.0), (1e-2, 6.0), (1.0, 6.0)])
-def test_decode_gqa_small(shape, lam, gain):
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_decode_gqa_small(shape, lam, gain, out):
     w = synth.small_workload("decode", d=128, dtype="bf16", bc=64, gain=gain, seed=44,
                              window=64, **shape)
-    _check_decode(w, lam)
+    _check_decode(w, lam, out=out)
 
 
-@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 1.0), (1e-2, 6.0)])
-def test_decode_gqa_b32_n65536(lam, gain):
+@pytest.mark.parametrize("lam,gain,out", [(0.0, 1.0, "bf16"), (1e-3, 1.0, "bf16"),
+                                          (1e-2, 6.0, "bf16"), (1e-2, 6.0, "fp32")])
+def test_decode_gqa_b32_n65536(lam, gain, out):
     w = synth.WORKLOADS[3].with_gain(gain)
-    res = _check_decode(w, lam, pairs=[(0, 0), (7, 3), (31, 7)])
+    res = _check_decode(w, lam, pairs=[(0, 0), (7, 3), (31, 7)], out=out)
     if gain > 1:
         assert res.skip_fraction > 0.3
 
@@ -196,16 +205,18 @@ def test_decode_gqa_b32_n65536(lam, gain):
     dict(B=1, Hq=16, Hkv=1, Nk=64),
 ])
 @pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-2, 6.0)])
-def test_decode_mla_small(shape, lam, gain):
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_decode_mla_small(shape, lam, gain, out):
     w = synth.small_workload("decode_mla", d=576, dv=512, dtype="bf16", bc=64, gain=gain,
                              seed=55, window=64, **shape)
-    _check_decode(w, lam)
+    _check_decode(w, lam, out=out)
 
 
-@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-2, 1.0), (1e-2, 6.0)])
-def test_decode_mla_b16_n32768(lam, gain):
+@pytest.mark.parametrize("lam,gain,out", [(0.0, 1.0, "bf16"), (1e-2, 1.0, "bf16"),
+                                          (1e-2, 6.0, "bf16"), (1e-2, 6.0, "fp32")])
+def test_decode_mla_b16_n32768(lam, gain, out):
     w = synth.WORKLOADS[5].with_gain(gain)
-    _check_decode(w, lam, pairs=[(0, 0), (15, 0)])
+    _check_decode(w, lam, pairs=[(0, 0), (15, 0)], out=out)
 
 
 # ----------------------------------------------------------------------------- behaviour

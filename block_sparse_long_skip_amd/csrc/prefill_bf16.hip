@@ -7,23 +7,40 @@
 // tile dropped whole when its max is far below the running max and its V never
 // read (paragraph beginning "BLASST предлагает"), tile 0 always processed
 // (first figure). The drop test is one scalar threshold on the running-max
-// statistics (digg thread "BLASST wins Best Paper at MLSys 2026").
+// statistics (digg thread "BLASST wins Best Paper at MLSys 2026"). The lazy
+// rescale below follows the FlashAttention 4 idea the post describes (the
+// paragraph on FlashAttention 4): partial sums are rescaled only when the
+// running max has grown enough to threaten precision, which keeps the result
+// exact; the drop decision always uses the exact running max.
 //
 // Layout. One workgroup of 4 waves per (batch, query head, query tile); wave w
 // owns query rows [32w, 32w+32). Scores are computed transposed,
 // S^T = K Q^T, so the MFMA result puts one query row in each lane column:
 // lane l holds row 32w + (l & 31) and 32 of the tile's 64 keys (lane l ^ 32
 // holds the other 32). Row max and row sum stay in-lane plus one lane swap.
-// The output is accumulated transposed too, O^T = V^T P^T, so the rescale by
-// exp(m_old - m_new) is a per-lane scalar. P^T feeds the second MFMA straight
-// from the first MFMA's accumulators (the key order inside one MFMA's
-// contraction is permuted to match the accumulator layout; the same
-// permutation is applied to V^T, so the sum is unchanged).
+// The output is accumulated transposed too, O^T = V^T P^T, so a rescale is a
+// per-lane scalar. P^T feeds the second MFMA straight from the first MFMA's
+// accumulators (the key order inside one MFMA's contraction is permuted to
+// match the accumulator layout; the same permutation is applied to V^T, so the
+// sum is unchanged). V^T comes from a row-major V tile through the gfx950
+// transposing LDS read (ds_read_b64_tr_b16).
 //
-// LDS: K tile row-major [64][128+8] bf16; V tile transposed [128][64+4] bf16
-// (written transposed from coalesced global loads). The skip vote is a wave
-// ballot over "this row keeps" plus an OR of the four waves' ballots through
-// LDS, so every wave takes the same branch and V is loaded only after it.
+// Pipeline (one barrier per key tile). At the top of iteration j the scores
+// S_j are in registers, the decision for tile j is known, the V_j loads into
+// LDS are in flight (kept tiles only) and K_{j+1} is in LDS. The iteration
+// issues the K_{j+2} loads, computes S_{j+1} on MFMA while the VALU turns S_j
+// into P_j, votes on tile j+1, waits for its own loads, meets the barrier,
+// issues the V_{j+1} loads only if tile j+1 is kept, and then runs
+// O^T += V_j^T P_j^T. Tiles travel global -> LDS without register staging.
+// So V is fetched only after the vote, and its latency hides behind a whole
+// tile of work. The vote for tile j+1 needs the running max before it, which
+// for lambda <= 1 is the plain prefix max of the row maxima (a dropped tile
+// cannot raise it), so it does not wait for the softmax of tile j.
+//
+// LDS: K and V tiles double-buffered, 64 rows x 256 B each, unpadded, with the
+// 16-byte chunk index XOR-swizzled by the row so that both the K operand reads
+// (16 rows, one chunk) and the transposing V reads (4 rows, 2 chunks) hit
+// distinct banks.
 #include "common.hpp"
 
 namespace blasst {
@@ -33,14 +50,57 @@ constexpr int D = 128;
 constexpr int BR = 128;
 constexpr int BC = 64;
 constexpr int NT = 256;
-constexpr int KP = D + 8;    // K tile pitch (bf16): 272 B rows, conflict-free b128 reads
-constexpr int VP = BC + 4;   // V^T tile pitch (bf16): 136 B rows
+constexpr int TILE_BYTES = BC * D * 2;  // 16 KB
+constexpr float kLazyRescaleLog2 = 8.f;  // rescale once the max grows by 2^8
+
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+
+// byte offset of (row, 16-byte chunk c) inside a 64 x 256 B tile
+__device__ __forceinline__ int swz(int row, int c) {
+  const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+  return row * 256 + ((c ^ f) << 4);
+}
+
+__device__ __forceinline__ s16x4_t ds_read_tr(const char* lds_byte_ptr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(lds_byte_ptr));
+}
+
+// Global -> LDS, no register staging (global_load_lds_dwordx4): wave w fills
+// rows 16w..16w+15 of a 64 x 256 B tile, 4 rows per instruction. Lane l lands
+// at (instruction base + 16 l), i.e. row 4r + l/16 and physical chunk l%16, so
+// it fetches the logical chunk that the swizzle maps there. Rows past the end
+// of the sequence are clamped to its last row: their scores are masked to
+// -inf, so they never contribute (P = 0 for them).
+__device__ __forceinline__ void tile_to_lds(char* tile, const uint16_t* base, int64_t stride,
+                                            int c0, int nk, int w, int lane) {
+  const int sub = lane >> 4, p = lane & 15;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int row = 16 * w + 4 * r + sub;
+    const int key = min(c0 + row, nk - 1);
+    const int f = ((row & 3) << 2) | ((row >> 2) & 3);
+    const uint16_t* src = base + (int64_t)key * stride + ((p ^ f) << 3);
+    __builtin_amdgcn_global_load_lds(
+        src, (__attribute__((address_space(3))) void*)(tile + (16 * w + 4 * r) * 256), 16, 0, 0);
+  }
+}
+
+// wait for this wave's outstanding global loads (including the ones into LDS)
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+struct RowState {
+  float m_prefix;  // exact running max (raw q.k units) of this lane's row, -inf before tile 0
+  float m_acc;     // reference max of the accumulators (<= m_prefix, within 2^8 in exp2 units)
+  float l;         // this lane's partial row sum (half of the row's keys)
+};
+
 }  // namespace
 
 __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * KP];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * VP];
-  __shared__ int votes[4];
+  __shared__ __attribute__((aligned(16))) char Ks[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(16))) char Vs[2][TILE_BYTES];
+  __shared__ int votes[2][4];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -68,6 +128,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const int last_row = min(i * BR + BR - 1, a.Nq - 1);
   const int first_pos = i * BR + (a.Nk - a.Nq);  // key position of the tile's first row
   const int J = a.causal ? min(a.nkt, (last_row + a.Nk - a.Nq) / BC + 1) : a.nkt;
+  const float c2 = a.scale_log2;
 
   // Q^T as the B operand: lane supplies Q[row][16kk + 8h .. +7]
   bf16x8_t qb[D / 16];
@@ -78,136 +139,191 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     qb[kk] = as_bf16x8(v);
   }
 
-  f32x16_t o[4];  // O^T[dv = 32db + 8(r/4) + 4h + r%4][row]
+  // S^T for one key tile from LDS: the two 32-key blocks are independent MFMA
+  // chains, interleaved, with each step's two K operands read one step ahead
+  auto scores = [&](const char* kt, f32x16_t (&s)[2]) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.f;
+    u32x4_t cur0 = *(const u32x4_t*)(kt + swz(l32, h));
+    u32x4_t cur1 = *(const u32x4_t*)(kt + swz(32 + l32, h));
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4_t nx0 = cur0, nx1 = cur1;
+      if (kk + 1 < D / 16) {
+        nx0 = *(const u32x4_t*)(kt + swz(l32, 2 * (kk + 1) + h));
+        nx1 = *(const u32x4_t*)(kt + swz(32 + l32, 2 * (kk + 1) + h));
+      }
+      s[0] = mfma32x32x16(as_bf16x8(cur0), qb[kk], s[0]);
+      s[1] = mfma32x32x16(as_bf16x8(cur1), qb[kk], s[1]);
+      cur0 = nx0;
+      cur1 = nx1;
+    }
+  };
+  // tiles that cross the end of the sequence or (causal) this tile's diagonal
+  auto tile_needs_mask = [&](int c0) {
+    return (c0 + BC > a.Nk) || (a.causal && c0 + BC - 1 > first_pos);
+  };
+  // masks keys past Nk and (causal) keys after this lane's row
+  auto mask_scores = [&](int c0, f32x16_t (&s)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int col = c0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+        if (col >= a.Nk || (a.causal && col > qpos)) s[kb][r] = kNegInf;
+      }
+  };
+  auto rowmax = [&](const f32x16_t (&s)[2]) {
+    float m0 = fmaxf(fmaxf(s[0][0], s[0][1]), s[0][2]);
+    float m1 = fmaxf(fmaxf(s[1][0], s[1][1]), s[1][2]);
+#pragma unroll
+    for (int r = 3; r < 15; r += 2) {
+      m0 = fmaxf(fmaxf(m0, s[0][r]), s[0][r + 1]);
+      m1 = fmaxf(fmaxf(m1, s[1][r]), s[1][r + 1]);
+    }
+    m0 = fmaxf(fmaxf(m0, s[0][15]), m1);
+    m0 = fmaxf(m0, s[1][15]);
+    return max_with_lane_xor32(m0);
+  };
+  // this lane's vote: keep unless its row's gap is below the threshold
+  auto lane_vote = [&](float mt, float m_before) {
+    float gap;
+    if (mt == kNegInf) gap = kNegInf;
+    else if (m_before == kNegInf) gap = __builtin_inff();
+    else gap = mt - m_before;
+    return valid && !(gap < a.thr_raw);
+  };
+
+  f32x16_t o[4];  // O^T[dv = 32db + 8(r/4) + 4h + r%4][row], relative to st.m_acc
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m = kNegInf, l = 0.f;
+  RowState st = {kNegInf, kNegInf, 0.f};
   int kept = 0;
   uint8_t* mrow = a.mask ? a.mask + ((int64_t)bh * a.nqt + i) * a.nkt : nullptr;
 
+  // ---- prologue: K_0, K_1 and V_0 (tile 0 is always kept) into LDS, then S_0
+  tile_to_lds(Ks[0], kp, a.ks2, 0, a.Nk, w, lane);
+  if (J > 1) tile_to_lds(Ks[1], kp, a.ks2, BC, a.Nk, w, lane);
+  tile_to_lds(Vs[0], vp, a.vs2, 0, a.Nk, w, lane);
+  wait_vmem();
+  __syncthreads();
+  f32x16_t s[2];
+  scores(Ks[0], s);
+  if (tile_needs_mask(0)) mask_scores(0, s);
+  float mt = rowmax(s);
+  bool keep = true;
+  if (mrow && t == 0) mrow[0] = 1;
+  __syncthreads();  // every wave has read K_0 before it is overwritten
+
   for (int j = 0; j < J; ++j) {
     const int c0 = j * BC;
-    __syncthreads();  // every wave is done with the previous K and V tiles
-    // K tile -> LDS: 64 rows x 16 chunks of 16 B; thread: chunk t&15 of rows t/16 + 16r
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int kr = (t >> 4) + 16 * r, kc = (t & 15) * 8;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (c0 + kr < a.Nk) v = load16(kp + (int64_t)(c0 + kr) * a.ks2 + kc);
-      store16(&Ks[kr * KP + kc], v);
+    const bool has_next = j + 1 < J;
+    // (a) K_{j+2} straight into the buffer K_j used (every wave read it before
+    //     the previous barrier)
+    if (j + 2 < J) tile_to_lds(Ks[j & 1], kp, a.ks2, c0 + 2 * BC, a.Nk, w, lane);
+    // (b) scores of tile j+1 (MFMA) ...
+    f32x16_t sn[2];
+    if (has_next) {
+      scores(Ks[(j + 1) & 1], sn);
+      if (tile_needs_mask(c0 + BC)) mask_scores(c0 + BC, sn);
     }
-    __syncthreads();
-
-    // S^T = K Q^T: s[kb][r] is key c0 + 32kb + 8(r/4) + 4h + r%4 for this lane's row
-    f32x16_t s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-#pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) {
-        bf16x8_t ka = as_bf16x8(*(const u32x4_t*)&Ks[(32 * kb + l32) * KP + 16 * kk + 8 * h]);
-        s[kb] = mfma32x32x16(ka, qb[kk], s[kb]);
-      }
-    }
-    // mask keys past Nk and (causal) keys after this row's position
-    const bool need_mask = (c0 + BC > a.Nk) || (a.causal && c0 + BC - 1 > first_pos);
-    if (need_mask) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int col = c0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (col >= a.Nk || (a.causal && col > qpos)) s[kb][r] = kNegInf;
-        }
-    }
-    float mt = kNegInf;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mt = fmaxf(mt, s[kb][r]);
-    mt = max_with_lane_xor32(mt);
-
-    // vote: the tile is dropped only when every valid row is below the threshold
-    float gap;
-    if (mt == kNegInf) gap = kNegInf;
-    else if (m == kNegInf) gap = __builtin_inff();
-    else gap = mt - m;
-    const bool lane_keep = valid && !(gap < a.thr_raw);
-    const bool wave_keep = __any(lane_keep);
-    if (lane == 0) votes[w] = wave_keep ? 1 : 0;
-    __syncthreads();
-    const bool keep = (j == 0) || (votes[0] | votes[1] | votes[2] | votes[3]);
-
+    // (c) ... while tile j's scores become P_j (VALU)
+    st.m_prefix = fmaxf(st.m_prefix, mt);  // running max through tile j
+    bf16x8_t pb[4];
     if (keep) {
-      // V tile, only now: thread loads rows 4g..4g+3 (g = t/16) of dv chunk t&15
-      // and writes them transposed, 4 keys (8 B) per dv row
-      {
-        const int g = t >> 4, cd = (t & 15) * 8;
-        u32x4_t vr[4];
+      // lazy rescale: move the accumulators' reference max only when the exact
+      // max has grown by more than 2^8 (any lane of the wave), or on the first tile
+      const bool grow = (st.m_prefix - st.m_acc) * c2 > kLazyRescaleLog2;
+      if (__any(grow)) {
+        const float alpha = fast_exp2((st.m_acc - st.m_prefix) * c2);
+        st.m_acc = st.m_prefix;
+        st.l *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int key = c0 + 4 * g + r;
-          vr[r] = (u32x4_t){0u, 0u, 0u, 0u};
-          if (key < a.Nk) vr[r] = load16(vp + (int64_t)key * a.vs2 + cd);
-        }
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          u32x2_t lo = {pack_lo16(vr[0][p], vr[1][p]), pack_lo16(vr[2][p], vr[3][p])};
-          u32x2_t hi = {pack_hi16(vr[0][p], vr[1][p]), pack_hi16(vr[2][p], vr[3][p])};
-          *(u32x2_t*)&Vt[(cd + 2 * p) * VP + 4 * g] = lo;
-          *(u32x2_t*)&Vt[(cd + 2 * p + 1) * VP + 4 * g] = hi;
-        }
+          for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
-      const float m_new = fmaxf(m, mt);
-      const float mc = (m_new == kNegInf) ? 0.f : m_new * a.scale_log2;
-      const float alpha = fast_exp2(m * a.scale_log2 - mc);
-      m = m_new;
-      // P^T (bf16) in the B-operand layout of chunk c: keys 16c + 8(e/4) + 4h + e%4
-      bf16x8_t pb[4];
-      float rs = 0.f;
+      const float mc = st.m_acc * c2;
+      // P^T (bf16) in the B-operand layout of chunk c: keys 16c + 8(e/4) + 4h + e%4.
+      // The row sum adds the fp32 values, so lse stays fp32-accurate.
+      float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         uint32_t pw[4];
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
-          const float p0 = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e], a.scale_log2, -mc));
-          const float p1 = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e + 1], a.scale_log2, -mc));
-          rs += p0 + p1;
+          const float p0 = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e], c2, -mc));
+          const float p1 = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e + 1], c2, -mc));
           pw[e >> 1] = pack_bf16x2(p0, p1);
+          ls0 += p0;
+          ls1 += p1;
         }
         pb[c] = as_bf16x8((u32x4_t){pw[0], pw[1], pw[2], pw[3]});
       }
-      l = l * alpha + rs;
+      st.l += ls0 + ls1;
+    }
+    // (e) vote on tile j+1 against the running max through tile j
+    float mtn = kNegInf;
+    if (has_next) {
+      mtn = rowmax(sn);
+      const bool wave_keep = __any(lane_vote(mtn, st.m_prefix));
+      if (lane == 0) votes[(j + 1) & 1][w] = wave_keep ? 1 : 0;
+    }
+    // (f) V_j (issued after tile j's vote) and K_{j+2} have landed in LDS
+    wait_vmem();
+    __syncthreads();
+    bool keep_next = false;
+    if (has_next) {
+      const int* vv = votes[(j + 1) & 1];
+      keep_next = (vv[0] | vv[1] | vv[2] | vv[3]) != 0;
+      if (mrow && t == 0) mrow[j + 1] = keep_next ? 1 : 0;
+      // (h) V_{j+1} is fetched only for a kept tile, into the buffer V_{j-1}
+      //     used (every wave finished reading it before this barrier)
+      if (keep_next) tile_to_lds(Vs[(j + 1) & 1], vp, a.vs2, c0 + BC, a.Nk, w, lane);
+    }
+    // (i) O^T += V_j^T P_j^T: per key chunk c, the 4 output blocks are
+    //     independent MFMA chains; the next chunk's V^T reads are issued first
+    if (keep) {
+      const char* vt = Vs[j & 1];
+      const int g16 = lane >> 4, jj = lane & 15;
+      auto vread = [&](int c, int db, u32x4_t& out) {
+        // lane group g16 reads keys 16c + 4h + jj/4 (and +8), 4 features from dv0
+        const int dv0 = 32 * db + 16 * (g16 & 1) + 4 * (jj & 3);
+        const int r0 = 16 * c + 4 * h + (jj >> 2);
+        const u32x2_t y0 = __builtin_bit_cast(u32x2_t, ds_read_tr(vt + swz(r0, dv0 >> 3) + ((dv0 & 7) << 1)));
+        const u32x2_t y1 =
+            __builtin_bit_cast(u32x2_t, ds_read_tr(vt + swz(r0 + 8, dv0 >> 3) + ((dv0 & 7) << 1)));
+        out = (u32x4_t){y0[0], y0[1], y1[0], y1[1]};
+      };
+      u32x4_t va[4], vb[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+      for (int db = 0; db < 4; ++db) vread(0, db, va[db]);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-      __syncthreads();  // V^T tile complete
-      // O^T += V^T P^T: A operand row dv = 32db + l32, keys 16c + 4h + {0..3} and 16c + 8 + 4h + {0..3}
+      for (int c = 0; c < 4; ++c) {
+        if (c + 1 < 4) {
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const uint16_t* vrow = &Vt[(32 * db + l32) * VP + 16 * c + 4 * h];
-          u32x2_t x0 = *(const u32x2_t*)vrow;
-          u32x2_t x1 = *(const u32x2_t*)(vrow + 8);
-          bf16x8_t va = as_bf16x8((u32x4_t){x0[0], x0[1], x1[0], x1[1]});
-          o[db] = mfma32x32x16(va, pb[c], o[db]);
+          for (int db = 0; db < 4; ++db) vread(c + 1, db, vb[db]);
         }
+#pragma unroll
+        for (int db = 0; db < 4; ++db) o[db] = mfma32x32x16(as_bf16x8(va[db]), pb[c], o[db]);
+#pragma unroll
+        for (int db = 0; db < 4; ++db) va[db] = vb[db];
       }
       ++kept;
     }
-    if (mrow && t == 0) mrow[j] = keep ? 1 : 0;
+    keep = keep_next;
+    mt = mtn;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s[kb] = sn[kb];
   }
   if (mrow) {
     for (int j = J + t; j < a.nkt; j += NT) mrow[j] = 2;
   }
 
   // epilogue: this lane and lane ^ 32 hold partial sums of the same row
-  const float lt = sum_with_lane_xor32(l);
+  const float lt = sum_with_lane_xor32(st.l);
   if (valid) {
     const float inv = 1.f / lt;
     const int64_t ob = b * a.os0 + hq * a.os1 + (int64_t)row * a.os2;
@@ -217,7 +333,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       for (int qd = 0; qd < 4; ++qd)
         store_out4(a.out, ob + 32 * db + 8 * qd + 4 * h, a.out_f32, o[db][4 * qd] * inv,
                    o[db][4 * qd + 1] * inv, o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv);
-    if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + row] = m * a.scale + logf(lt);
+    if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + row] = st.m_acc * a.scale + logf(lt);
   }
   if (a.stats && t == 0) {
     atomicAdd((unsigned long long*)&a.stats[2 * bh], (unsigned long long)J);

@@ -148,6 +148,9 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
                 "no prefill kernel for dtype=%d d_qk=%d d_v=%d br=%d bc=%d (supported: fp32 "
                 "64/64 64x64, bf16 128/128 128x64)",
                 (int)dtype, s.d_qk, s.d_v, br, bc);
+  // the bf16 kernel addresses a 64-row tile with 32-bit per-lane byte offsets
+  if (b16 && (s.k_stride[2] > (1 << 24) || s.v_stride[2] > (1 << 24)))
+    return fail(BLASST_E_UNSUPPORTED, "bf16 prefill needs key/value position strides <= 2^24 elements");
   const int64_t nqt = ((int64_t)s.len_q + br - 1) / br;
   const int64_t nkt = ((int64_t)s.len_kv + bc - 1) / bc;
   if ((int64_t)s.batch * s.heads_q * nqt > 0x7fffffffLL)

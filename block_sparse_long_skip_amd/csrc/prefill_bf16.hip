@@ -31,7 +31,7 @@
 // issues the K_{j+2} loads, computes S_{j+1} on MFMA while the VALU turns S_j
 // into P_j, votes on tile j+1, waits for its own loads, meets the barrier,
 // issues the V_{j+1} loads only if tile j+1 is kept, and then runs
-// O^T += V_j^T P_j^T. Tiles travel global -> LDS without register staging.
+// O^T += V_j^T P_j^T.
 // So V is fetched only after the vote, and its latency hides behind a whole
 // tile of work. The vote for tile j+1 needs the running max before it, which
 // for lambda <= 1 is the plain prefix max of the row maxima (a dropped tile
@@ -40,7 +40,12 @@
 // LDS: K and V tiles double-buffered, 64 rows x 256 B each, unpadded, with the
 // 16-byte chunk index XOR-swizzled by the row so that both the K operand reads
 // (16 rows, one chunk) and the transposing V reads (4 rows, 2 chunks) hit
-// distinct banks.
+// distinct banks. Tiles travel global -> LDS with global_load_lds_dwordx4 (no
+// register staging). Every per-lane address is computed once before the loop:
+// LDS reads are a per-lane base plus immediate offsets, tile loads a uniform
+// tile pointer plus a per-lane 32-bit offset.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace blasst {
@@ -55,35 +60,19 @@ constexpr float kLazyRescaleLog2 = 8.f;  // rescale once the max grows by 2^8
 
 typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 
+// XOR applied to the 16-byte chunk index of tile row `row`
+__device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 // byte offset of (row, 16-byte chunk c) inside a 64 x 256 B tile
-__device__ __forceinline__ int swz(int row, int c) {
-  const int f = ((row & 3) << 2) | ((row >> 2) & 3);
-  return row * 256 + ((c ^ f) << 4);
+__device__ __forceinline__ int swz(int row, int c) { return row * 256 + ((c ^ swz_f(row)) << 4); }
+
+__device__ __forceinline__ u32x2_t ds_read_tr(const char* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) s16x4_t*)(p)));
 }
 
-__device__ __forceinline__ s16x4_t ds_read_tr(const char* lds_byte_ptr) {
-  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4_t*)(lds_byte_ptr));
-}
-
-// Global -> LDS, no register staging (global_load_lds_dwordx4): wave w fills
-// rows 16w..16w+15 of a 64 x 256 B tile, 4 rows per instruction. Lane l lands
-// at (instruction base + 16 l), i.e. row 4r + l/16 and physical chunk l%16, so
-// it fetches the logical chunk that the swizzle maps there. Rows past the end
-// of the sequence are clamped to its last row: their scores are masked to
-// -inf, so they never contribute (P = 0 for them).
-__device__ __forceinline__ void tile_to_lds(char* tile, const uint16_t* base, int64_t stride,
-                                            int c0, int nk, int w, int lane) {
-  const int sub = lane >> 4, p = lane & 15;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int row = 16 * w + 4 * r + sub;
-    const int key = min(c0 + row, nk - 1);
-    const int f = ((row & 3) << 2) | ((row >> 2) & 3);
-    const uint16_t* src = base + (int64_t)key * stride + ((p ^ f) << 3);
-    __builtin_amdgcn_global_load_lds(
-        src, (__attribute__((address_space(3))) void*)(tile + (16 * w + 4 * r) * 256), 16, 0, 0);
-  }
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds_row_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_row_base, 16,
+                                   0, 0);
 }
 
 // wait for this wave's outstanding global loads (including the ones into LDS)
@@ -119,8 +108,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const int kvh = hq / (a.Hq / a.Hkv);
 
   const uint16_t* qp = (const uint16_t*)a.q + b * a.qs0 + hq * a.qs1;
-  const uint16_t* kp = (const uint16_t*)a.k + b * a.ks0 + kvh * a.ks1;
-  const uint16_t* vp = (const uint16_t*)a.v + b * a.vs0 + kvh * a.vs1;
+  const char* kp = (const char*)((const uint16_t*)a.k + b * a.ks0 + kvh * a.ks1);
+  const char* vp = (const char*)((const uint16_t*)a.v + b * a.vs0 + kvh * a.vs1);
 
   const int row = i * BR + 32 * w + l32;  // this lane's query row
   const bool valid = row < a.Nq;
@@ -139,19 +128,66 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     qb[kk] = as_bf16x8(v);
   }
 
+  // ---- per-lane addresses, computed once
+  // Tile loads: wave w fills rows 16w..16w+15, 4 rows per instruction; lane l
+  // lands at (instruction base + 16 l) = row 4r + l/16, physical chunk l%16, so
+  // it fetches the logical chunk the swizzle maps there.
+  const int sub = lane >> 4, pch = lane & 15;
+  uint32_t koff[4], voff[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int trow = 16 * w + 4 * r + sub;
+    const int ch = pch ^ swz_f(trow);
+    koff[r] = (uint32_t)(((int64_t)trow * a.ks2 + ch * 8) * 2);
+    voff[r] = (uint32_t)(((int64_t)trow * a.vs2 + ch * 8) * 2);
+  }
+  // One tile into LDS. Rows past the end of the sequence are clamped to its
+  // last row: their scores are masked to -inf, so they never contribute.
+  auto tile_to_lds = [&](char* tile, const char* base, const uint32_t (&off)[4], int64_t stride,
+                         int c0) {
+    if (c0 + BC <= a.Nk) {
+      const char* tp = base + (int64_t)c0 * stride * 2;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) lds_dma16(tp + off[r], tile + (16 * w + 4 * r) * 256);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int trow = 16 * w + 4 * r + sub;
+        const int key = min(c0 + trow, a.Nk - 1);
+        const int ch = pch ^ swz_f(trow);
+        lds_dma16(base + ((int64_t)key * stride + ch * 8) * 2, tile + (16 * w + 4 * r) * 256);
+      }
+    }
+  };
+  // K operand reads: key row 32kb + l32, chunk 2kk + h (kb = 1 is +8192 bytes)
+  int kro[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) kro[kk] = swz(l32, 2 * kk + h);
+  // V^T operand reads (transposing): lane group g16 = lane/16 reads keys
+  // 16c + 4h + jj/4 and +8 (key chunk c is +4096 bytes), features dv0..dv0+3
+  const int g16 = lane >> 4, jj = lane & 15;
+  int vro[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db) {
+    const int dv0 = 32 * db + 16 * (g16 & 1) + 4 * (jj & 3);
+    const int r0 = 4 * h + (jj >> 2);
+    vro[db][0] = swz(r0, dv0 >> 3) + ((dv0 & 7) << 1);
+    vro[db][1] = swz(r0 + 8, dv0 >> 3) + ((dv0 & 7) << 1);
+  }
+
   // S^T for one key tile from LDS: the two 32-key blocks are independent MFMA
   // chains, interleaved, with each step's two K operands read one step ahead
   auto scores = [&](const char* kt, f32x16_t (&s)[2]) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.f;
-    u32x4_t cur0 = *(const u32x4_t*)(kt + swz(l32, h));
-    u32x4_t cur1 = *(const u32x4_t*)(kt + swz(32 + l32, h));
+    u32x4_t cur0 = *(const u32x4_t*)(kt + kro[0]);
+    u32x4_t cur1 = *(const u32x4_t*)(kt + 8192 + kro[0]);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       u32x4_t nx0 = cur0, nx1 = cur1;
       if (kk + 1 < D / 16) {
-        nx0 = *(const u32x4_t*)(kt + swz(l32, 2 * (kk + 1) + h));
-        nx1 = *(const u32x4_t*)(kt + swz(32 + l32, 2 * (kk + 1) + h));
+        nx0 = *(const u32x4_t*)(kt + kro[kk + 1]);
+        nx1 = *(const u32x4_t*)(kt + 8192 + kro[kk + 1]);
       }
       s[0] = mfma32x32x16(as_bf16x8(cur0), qb[kk], s[0]);
       s[1] = mfma32x32x16(as_bf16x8(cur1), qb[kk], s[1]);
@@ -204,29 +240,31 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   uint8_t* mrow = a.mask ? a.mask + ((int64_t)bh * a.nqt + i) * a.nkt : nullptr;
 
   // ---- prologue: K_0, K_1 and V_0 (tile 0 is always kept) into LDS, then S_0
-  tile_to_lds(Ks[0], kp, a.ks2, 0, a.Nk, w, lane);
-  if (J > 1) tile_to_lds(Ks[1], kp, a.ks2, BC, a.Nk, w, lane);
-  tile_to_lds(Vs[0], vp, a.vs2, 0, a.Nk, w, lane);
+  tile_to_lds(Ks[0], kp, koff, a.ks2, 0);
+  if (J > 1) tile_to_lds(Ks[1], kp, koff, a.ks2, BC);
+  tile_to_lds(Vs[0], vp, voff, a.vs2, 0);
   wait_vmem();
   __syncthreads();
-  f32x16_t s[2];
-  scores(Ks[0], s);
-  if (tile_needs_mask(0)) mask_scores(0, s);
-  float mt = rowmax(s);
+  f32x16_t sA[2], sB[2];
+  scores(Ks[0], sA);
+  if (tile_needs_mask(0)) mask_scores(0, sA);
+  float mt = rowmax(sA);
   bool keep = true;
   if (mrow && t == 0) mrow[0] = 1;
   __syncthreads();  // every wave has read K_0 before it is overwritten
 
-  for (int j = 0; j < J; ++j) {
+  int j = 0;
+  // one key tile; P = j & 1 (compile-time), s = S_j, sn receives S_{j+1}
+  auto step = [&](auto PAR, f32x16_t (&s)[2], f32x16_t (&sn)[2]) {
+    constexpr int P = decltype(PAR)::value;
     const int c0 = j * BC;
     const bool has_next = j + 1 < J;
     // (a) K_{j+2} straight into the buffer K_j used (every wave read it before
     //     the previous barrier)
-    if (j + 2 < J) tile_to_lds(Ks[j & 1], kp, a.ks2, c0 + 2 * BC, a.Nk, w, lane);
+    if (j + 2 < J) tile_to_lds(Ks[P], kp, koff, a.ks2, c0 + 2 * BC);
     // (b) scores of tile j+1 (MFMA) ...
-    f32x16_t sn[2];
     if (has_next) {
-      scores(Ks[(j + 1) & 1], sn);
+      scores(Ks[P ^ 1], sn);
       if (tile_needs_mask(c0 + BC)) mask_scores(c0 + BC, sn);
     }
     // (c) ... while tile j's scores become P_j (VALU)
@@ -269,42 +307,39 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     if (has_next) {
       mtn = rowmax(sn);
       const bool wave_keep = __any(lane_vote(mtn, st.m_prefix));
-      if (lane == 0) votes[(j + 1) & 1][w] = wave_keep ? 1 : 0;
+      if (lane == 0) votes[P ^ 1][w] = wave_keep ? 1 : 0;
     }
     // (f) V_j (issued after tile j's vote) and K_{j+2} have landed in LDS
     wait_vmem();
     __syncthreads();
     bool keep_next = false;
     if (has_next) {
-      const int* vv = votes[(j + 1) & 1];
+      const int* vv = votes[P ^ 1];
       keep_next = (vv[0] | vv[1] | vv[2] | vv[3]) != 0;
       if (mrow && t == 0) mrow[j + 1] = keep_next ? 1 : 0;
       // (h) V_{j+1} is fetched only for a kept tile, into the buffer V_{j-1}
       //     used (every wave finished reading it before this barrier)
-      if (keep_next) tile_to_lds(Vs[(j + 1) & 1], vp, a.vs2, c0 + BC, a.Nk, w, lane);
+      if (keep_next) tile_to_lds(Vs[P ^ 1], vp, voff, a.vs2, c0 + BC);
     }
     // (i) O^T += V_j^T P_j^T: per key chunk c, the 4 output blocks are
     //     independent MFMA chains; the next chunk's V^T reads are issued first
     if (keep) {
-      const char* vt = Vs[j & 1];
-      const int g16 = lane >> 4, jj = lane & 15;
-      auto vread = [&](int c, int db, u32x4_t& out) {
-        // lane group g16 reads keys 16c + 4h + jj/4 (and +8), 4 features from dv0
-        const int dv0 = 32 * db + 16 * (g16 & 1) + 4 * (jj & 3);
-        const int r0 = 16 * c + 4 * h + (jj >> 2);
-        const u32x2_t y0 = __builtin_bit_cast(u32x2_t, ds_read_tr(vt + swz(r0, dv0 >> 3) + ((dv0 & 7) << 1)));
-        const u32x2_t y1 =
-            __builtin_bit_cast(u32x2_t, ds_read_tr(vt + swz(r0 + 8, dv0 >> 3) + ((dv0 & 7) << 1)));
-        out = (u32x4_t){y0[0], y0[1], y1[0], y1[1]};
-      };
+      const char* vt = Vs[P];
       u32x4_t va[4], vb[4];
 #pragma unroll
-      for (int db = 0; db < 4; ++db) vread(0, db, va[db]);
+      for (int db = 0; db < 4; ++db) {
+        const u32x2_t y0 = ds_read_tr(vt + vro[db][0]), y1 = ds_read_tr(vt + vro[db][1]);
+        va[db] = (u32x4_t){y0[0], y0[1], y1[0], y1[1]};
+      }
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         if (c + 1 < 4) {
 #pragma unroll
-          for (int db = 0; db < 4; ++db) vread(c + 1, db, vb[db]);
+          for (int db = 0; db < 4; ++db) {
+            const u32x2_t y0 = ds_read_tr(vt + 4096 * (c + 1) + vro[db][0]);
+            const u32x2_t y1 = ds_read_tr(vt + 4096 * (c + 1) + vro[db][1]);
+            vb[db] = (u32x4_t){y0[0], y0[1], y1[0], y1[1]};
+          }
         }
 #pragma unroll
         for (int db = 0; db < 4; ++db) o[db] = mfma32x32x16(as_bf16x8(va[db]), pb[c], o[db]);
@@ -315,11 +350,17 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     }
     keep = keep_next;
     mt = mtn;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s[kb] = sn[kb];
+    ++j;
+  };
+  const std::integral_constant<int, 0> even;
+  const std::integral_constant<int, 1> odd;
+  while (j < J) {
+    step(even, sA, sB);
+    if (j >= J) break;
+    step(odd, sB, sA);
   }
   if (mrow) {
-    for (int j = J + t; j < a.nkt; j += NT) mrow[j] = 2;
+    for (int x = J + t; x < a.nkt; x += NT) mrow[x] = 2;
   }
 
   // epilogue: this lane and lane ^ 32 hold partial sums of the same row

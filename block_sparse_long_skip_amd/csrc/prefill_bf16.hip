@@ -195,6 +195,54 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       cur1 = nx1;
     }
   };
+  // P_j (bf16, B-operand layout of chunk c: keys 16c + 8(e/4) + 4h + e%4)
+  // from S_j: the four values of step x = 4c' + ... live in pw; the row sum
+  // adds the fp32 values so lse stays fp32-accurate
+  auto probs_step = [&](const f32x16_t (&s)[2], float mc, int x, uint32_t (&pw)[4][4],
+                        float& ls0, float& ls1) {
+    const int c = x >> 1, e0 = 4 * (x & 1);
+    const float p0 = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e0], c2, -mc));
+    const float p1 = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e0 + 1], c2, -mc));
+    const float p2 = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e0 + 2], c2, -mc));
+    const float p3 = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e0 + 3], c2, -mc));
+    pw[c][2 * (x & 1)] = pack_bf16x2(p0, p1);
+    pw[c][2 * (x & 1) + 1] = pack_bf16x2(p2, p3);
+    ls0 += p0 + p2;
+    ls1 += p1 + p3;
+  };
+  // S_{j+1} on MFMA and P_j on the VALU, interleaved in program order: each of
+  // the 8 steps issues the next step's two K-operand reads, two MFMAs (one per
+  // 32-key block) and a quarter-chunk of P_j; the scheduling fence keeps that
+  // order, so a wave fills its own MFMA dependency stalls with softmax work
+  auto scores_and_probs = [&](const char* kt, f32x16_t (&sn)[2], const f32x16_t (&s)[2],
+                              float mc, bf16x8_t (&pb)[4], float& lsum) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sn[0][r] = sn[1][r] = 0.f;
+    uint32_t pw[4][4];
+    float ls0 = 0.f, ls1 = 0.f;
+    u32x4_t cur0 = *(const u32x4_t*)(kt + kro[0]);
+    u32x4_t cur1 = *(const u32x4_t*)(kt + 8192 + kro[0]);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      u32x4_t nx0 = cur0, nx1 = cur1;
+      if (kk + 1 < D / 16) {
+        nx0 = *(const u32x4_t*)(kt + kro[kk + 1]);
+        nx1 = *(const u32x4_t*)(kt + 8192 + kro[kk + 1]);
+      }
+      sn[0] = mfma32x32x16(as_bf16x8(cur0), qb[kk], sn[0]);
+      sn[1] = mfma32x32x16(as_bf16x8(cur1), qb[kk], sn[1]);
+      probs_step(s, mc, kk, pw, ls0, ls1);
+      // consume this step's results here so they are not sunk past the MFMAs
+      asm volatile("" ::"v"(pw[kk >> 1][2 * (kk & 1)]), "v"(pw[kk >> 1][2 * (kk & 1) + 1]),
+                   "v"(ls0), "v"(ls1));
+      cur0 = nx0;
+      cur1 = nx1;
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int c = 0; c < 4; ++c) pb[c] = as_bf16x8((u32x4_t){pw[c][0], pw[c][1], pw[c][2], pw[c][3]});
+    lsum += ls0 + ls1;
+  };
   // tiles that cross the end of the sequence or (causal) this tile's diagonal
   auto tile_needs_mask = [&](int c0) {
     return (c0 + BC > a.Nk) || (a.causal && c0 + BC - 1 > first_pos);
@@ -262,12 +310,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     // (a) K_{j+2} straight into the buffer K_j used (every wave read it before
     //     the previous barrier)
     if (j + 2 < J) tile_to_lds(Ks[P], kp, koff, a.ks2, c0 + 2 * BC);
-    // (b) scores of tile j+1 (MFMA) ...
-    if (has_next) {
-      scores(Ks[P ^ 1], sn);
-      if (tile_needs_mask(c0 + BC)) mask_scores(c0 + BC, sn);
-    }
-    // (c) ... while tile j's scores become P_j (VALU)
+    // (b, c) scores of tile j+1 (MFMA) and P_j (VALU)
     st.m_prefix = fmaxf(st.m_prefix, mt);  // running max through tile j
     bf16x8_t pb[4];
     if (keep) {
@@ -283,25 +326,22 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
-      const float mc = st.m_acc * c2;
-      // P^T (bf16) in the B-operand layout of chunk c: keys 16c + 8(e/4) + 4h + e%4.
-      // The row sum adds the fp32 values, so lse stays fp32-accurate.
+    }
+    const float mc = st.m_acc * c2;
+    if (has_next && keep) {
+      scores_and_probs(Ks[P ^ 1], sn, s, mc, pb, st.l);
+    } else if (has_next) {
+      scores(Ks[P ^ 1], sn);
+    } else if (keep) {
+      uint32_t pw[4][4];
       float ls0 = 0.f, ls1 = 0.f;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        uint32_t pw[4];
+      for (int x = 0; x < 8; ++x) probs_step(s, mc, x, pw, ls0, ls1);
 #pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const float p0 = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e], c2, -mc));
-          const float p1 = fast_exp2(fmaf(s[c >> 1][8 * (c & 1) + e + 1], c2, -mc));
-          pw[e >> 1] = pack_bf16x2(p0, p1);
-          ls0 += p0;
-          ls1 += p1;
-        }
-        pb[c] = as_bf16x8((u32x4_t){pw[0], pw[1], pw[2], pw[3]});
-      }
+      for (int c = 0; c < 4; ++c) pb[c] = as_bf16x8((u32x4_t){pw[c][0], pw[c][1], pw[c][2], pw[c][3]});
       st.l += ls0 + ls1;
     }
+    if (has_next && tile_needs_mask(c0 + BC)) mask_scores(c0 + BC, sn);
     // (e) vote on tile j+1 against the running max through tile j
     float mtn = kNegInf;
     if (has_next) {

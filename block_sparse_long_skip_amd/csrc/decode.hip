@@ -1,5 +1,6 @@
 // bf16 skip-softmax decode on gfx950: one query token per (batch, head)
-// against a contiguous KV cache, 64-key tiles.
+// against a contiguous KV cache with separate values, 64-key tiles (the latent
+// cache kernel lives in decode_mla.hip).
 //
 // Method: BLASST post (seeallochnaya, "BLASST: Dynamic BLocked Attention
 // Sparsity via Softmax Thresholding"): key tiles in increasing order, online
@@ -20,12 +21,6 @@
 //   O^T += V^T P^T runs on MFMA. Each wave keeps its own (m, l, O) partial;
 //   a log-sum-exp merge across the 8 waves ends the kernel.
 //
-// decode_mla_kernel (latent cache: d_qk = 576, values = first 512 features of
-//   each key): one workgroup of 4 waves per (batch, KV head, group of 16 query
-//   heads). The whole 64x576 key tile is staged in LDS once and serves both
-//   the scores (wave w scores keys 16w..16w+15) and, for kept tiles, P.V (wave
-//   w produces output features 128w..128w+127). Skipping saves the exp, the
-//   row sums and the P.V MFMAs; the latent bytes are read regardless.
 #include "common.hpp"
 
 namespace blasst {
@@ -37,15 +32,6 @@ constexpr int GD = 128;
 constexpr int GNW = 8;
 constexpr int GNT = GNW * 64;
 constexpr int GVP = BC + 8;  // V^T slice pitch (bf16): 144 B rows
-// MLA
-constexpr int MDQK = 576;
-constexpr int MDV = 512;
-static_assert(MDV % 128 == 0 && MDV / 128 == 4, "4 waves x 128 output features");
-constexpr int MNW = 4;
-constexpr int MNT = MNW * 64;
-constexpr int MKP = MDQK + 8;  // K tile pitch (bf16): 1168 B rows
-constexpr int MPP = BC + 8;    // P^T pitch
-constexpr int HG = 16;         // query heads per MLA workgroup
 }  // namespace
 
 __global__ void __launch_bounds__(GNT) decode_gqa_kernel(DecodeArgs a) {
@@ -255,180 +241,11 @@ __global__ void __launch_bounds__(GNT) decode_gqa_kernel(DecodeArgs a) {
   }
 }
 
-__global__ void __launch_bounds__(MNT) decode_mla_kernel(DecodeArgs a, int ngroups) {
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BC * MKP];
-  __shared__ __attribute__((aligned(16))) uint16_t Ps[HG * MPP];
-  __shared__ float tmw[MNW][HG];
-  __shared__ float lred[MNW][HG];
-
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int w = t >> 6;
-  const int n = lane & 15;
-  const int g = lane >> 4;
-  // consecutive logical blocks share a sequence; when the grid is a multiple
-  // of 8 they are placed on one XCD so the latent tiles are shared in its L2
-  const int total = (int)gridDim.x;
-  int lb = (int)blockIdx.x;
-  if ((total & 7) == 0) lb = (lb & 7) * (total >> 3) + (lb >> 3);
-  const int gi = lb % ngroups;
-  const int seq = lb / ngroups;  // (b, kvh)
-  const int b = seq / a.Hkv, kvh = seq % a.Hkv;
-  const int G = a.G;
-  const int h0 = gi * HG;
-  const bool hvalid = h0 + n < G;
-  const int hq = kvh * G + h0 + n;
-
-  const uint16_t* qp = (const uint16_t*)a.q + b * a.qs0 + (int64_t)hq * a.qs1;
-  const uint16_t* kp = (const uint16_t*)a.k + b * a.ks0 + kvh * a.ks1;
-
-  bf16x8_t qb[MDQK / 32];
-#pragma unroll
-  for (int kk = 0; kk < MDQK / 32; ++kk) {
-    u32x4_t v = {0u, 0u, 0u, 0u};
-    if (hvalid) v = load16(qp + 32 * kk + 8 * g);
-    qb[kk] = as_bf16x8(v);
-  }
-  f32x4_t o[8];  // O^T[dv = 128w + 16db + 4g + i][head n]
-#pragma unroll
-  for (int db = 0; db < 8; ++db) o[db] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float m = kNegInf, lp = 0.f;
-  int kept = 0;
-
-  for (int j = 0; j < a.nkt; ++j) {
-    const int c0 = j * BC;
-    __syncthreads();
-    for (int idx = t; idx < BC * (MDQK / 8); idx += MNT) {
-      const int kr = idx / (MDQK / 8), ch = (idx % (MDQK / 8)) * 8;
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (c0 + kr < a.Nk) v = load16(kp + (int64_t)(c0 + kr) * a.ks2 + ch);
-      store16(&Ks[kr * MKP + ch], v);
-    }
-    __syncthreads();
-    f32x4_t s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kk = 0; kk < MDQK / 32; ++kk) {
-      bf16x8_t ka = as_bf16x8(*(const u32x4_t*)&Ks[(16 * w + (lane & 15)) * MKP + 32 * kk + 8 * g]);
-      s = mfma16x16x32(ka, qb[kk], s);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (c0 + 16 * w + 4 * g + i >= a.Nk) s[i] = kNegInf;
-    float tm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
-    tm = fmaxf(tm, shfl_xor_f(tm, 16));
-    tm = fmaxf(tm, shfl_xor_f(tm, 32));
-    if (g == 0) tmw[w][n] = tm;
-    __syncthreads();
-    const float TM = fmaxf(fmaxf(tmw[0][n], tmw[1][n]), fmaxf(tmw[2][n], tmw[3][n]));
-    float gap;
-    if (TM == kNegInf) gap = kNegInf;
-    else if (m == kNegInf) gap = __builtin_inff();
-    else gap = TM - m;
-    const bool keep = hvalid && ((j == 0) || !(gap < a.thr_raw));
-    if (a.mask && w == 0 && g == 0 && hvalid)
-      a.mask[((int64_t)b * a.Hq + hq) * a.nkt + j] = keep ? 1 : 0;
-    kept += keep ? 1 : 0;
-    if (__any(keep)) {  // same in every wave: TM and m are replicated
-      float p[4] = {0.f, 0.f, 0.f, 0.f};
-      if (keep) {
-        const float m_new = fmaxf(m, TM);
-        const float mc = m_new * a.scale_log2;
-        const float alpha = fast_exp2(m * a.scale_log2 - mc);
-        m = m_new;
-        lp *= alpha;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) o[db] *= alpha;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          p[i] = fast_exp2(fmaf(s[i], a.scale_log2, -mc));
-          lp += p[i];
-        }
-      }
-      u32x2_t pw = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
-      *(u32x2_t*)&Ps[n * MPP + 16 * w + 4 * g] = pw;
-      __syncthreads();
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        const bf16x8_t pbv = as_bf16x8(*(const u32x4_t*)&Ps[n * MPP + 32 * cc + 8 * g]);
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          const int dv = 128 * w + 16 * db + (lane & 15);
-          const uint16_t* col = &Ks[(32 * cc + 8 * g) * MKP + dv];
-          uint32_t x[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            x[e] = (uint32_t)col[(2 * e) * MKP] | ((uint32_t)col[(2 * e + 1) * MKP] << 16);
-          o[db] = mfma16x16x32(as_bf16x8((u32x4_t){x[0], x[1], x[2], x[3]}), pbv, o[db]);
-        }
-      }
-    }
-  }
-
-  // row sums: lanes (n, g) of every wave hold partials for head n
-  lp += shfl_xor_f(lp, 16);
-  lp += shfl_xor_f(lp, 32);
-  if (g == 0) lred[w][n] = lp;
-  __syncthreads();
-  const float L = lred[0][n] + lred[1][n] + lred[2][n] + lred[3][n];
-  if (hvalid) {
-    const float inv = 1.f / L;
-    const int64_t ob = b * a.os0 + (int64_t)hq * a.os1;
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-      store_out4(a.out, ob + 128 * w + 16 * db + 4 * g, a.out_f32, o[db][0] * inv, o[db][1] * inv,
-                 o[db][2] * inv, o[db][3] * inv);
-    if (w == 0 && g == 0) {
-      if (a.lse) a.lse[(int64_t)b * a.Hq + hq] = m * a.scale + logf(L);
-      if (a.stats) {
-        int64_t* st = a.stats + ((int64_t)b * a.Hq + hq) * 3;
-        st[0] = a.nkt;
-        st[1] = kept;
-      }
-    }
-  }
-}
-
-// stats[..., 2] for a latent cache: the number of key tiles that at least one
-// query head of the KV head keeps, counted from the mask. One block per (b, kvh).
-__global__ void __launch_bounds__(256) decode_vtiles_kernel(const uint8_t* mask, int64_t* stats,
-                                                            int Hq, int Hkv, int G, int nkt) {
-  __shared__ int total;
-  const int b = blockIdx.x / Hkv, kvh = blockIdx.x % Hkv;
-  if (threadIdx.x == 0) total = 0;
-  __syncthreads();
-  int cntv = 0;
-  for (int j = threadIdx.x; j < nkt; j += blockDim.x) {
-    bool any = false;
-    for (int h = 0; h < G; ++h)
-      any |= mask[((int64_t)b * Hq + kvh * G + h) * nkt + j] == 1;
-    cntv += any ? 1 : 0;
-  }
-  atomicAdd(&total, cntv);
-  __syncthreads();
-  for (int h = threadIdx.x; h < G; h += blockDim.x)
-    stats[((int64_t)b * Hq + kvh * G + h) * 3 + 2] = total;
-}
-
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t stream) {
   const int64_t nblocks = (int64_t)a.B * a.Hkv;
   if (nblocks == 0) return hipSuccess;
   hipLaunchKernelGGL(decode_gqa_kernel, dim3((unsigned)nblocks), dim3(GNT), 0, stream, a);
   return hipGetLastError();
-}
-
-hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t stream) {
-  const int ngroups = (a.G + HG - 1) / HG;
-  const int64_t nblocks = (int64_t)a.B * a.Hkv * ngroups;
-  if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_mla_kernel, dim3((unsigned)nblocks), dim3(MNT), 0, stream, a, ngroups);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.stats && a.mask) {
-    hipLaunchKernelGGL(decode_vtiles_kernel, dim3((unsigned)(a.B * a.Hkv)), dim3(256), 0, stream,
-                       a.mask, a.stats, a.Hq, a.Hkv, a.G, a.nkt);
-    e = hipGetLastError();
-  }
-  return e;
 }
 
 }  // namespace blasst

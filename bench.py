@@ -197,6 +197,9 @@ def bench_decode(args):
             q, k = to_device(inp.q, w), to_device(inp.k, w)
             v = to_device(inp.v, w) if inp.v is not None else None
             del inp
+            nws = A.decode_workspace_size(w.B, w.Hq, w.Hkv, w.Nk, w.d, w.dv, latent=v is None,
+                                          bc=w.bc)
+            ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
             for lam in w.lambdas:
                 times = []
                 res = None
@@ -204,7 +207,7 @@ def bench_decode(args):
                     flush.fill_(it)
                     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     s.record()
-                    res = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv)
+                    res = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv, workspace=ws)
                     e.record()
                     torch.cuda.synchronize()
                     if it > 0:
@@ -225,7 +228,7 @@ def bench_decode(args):
                                                         if v is not None else None)))
                 log(f"[bench]   {kind} gain {gain} lam {lam}: {ms:.3f} ms {gbs:.0f} GB/s "
                     f"skip {res.skip_fraction:.3f}")
-            del q, k, v
+            del q, k, v, ws
             torch.cuda.empty_cache()
         results[kind] = rows
     del flush
@@ -288,11 +291,16 @@ def only(args):
     inp = synth.make_inputs(w)
     q, k = to_device(inp.q, w), to_device(inp.k, w)
     v = to_device(inp.v, w) if inp.v is not None else None
+    ws = None
+    if w.kind != "prefill":
+        nws = A.decode_workspace_size(w.B, w.Hq, w.Hkv, w.Nk, w.d, w.dv, latent=v is None,
+                                      bc=w.bc)
+        ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
     for _ in range(args.steps):
         if w.kind == "prefill":
             A.prefill(q, k, v, args.lam, causal=True, br=w.br, bc=w.bc, want_stats=False)
         else:
-            A.decode(q, k, v, args.lam, bc=w.bc, dv=w.dv, want_stats=False)
+            A.decode(q, k, v, args.lam, bc=w.bc, dv=w.dv, want_stats=False, workspace=ws)
     torch.cuda.synchronize()
     log(f"[bench] launched {args.only} x {args.steps}")
 

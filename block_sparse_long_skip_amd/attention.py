@@ -25,12 +25,12 @@ BLASST_BF16 = 1
 STATUS = {
     0: "BLASST_OK", 1: "BLASST_E_NULL", 2: "BLASST_E_SHAPE", 3: "BLASST_E_DTYPE",
     4: "BLASST_E_LAMBDA", 5: "BLASST_E_ALIGN", 6: "BLASST_E_UNSUPPORTED", 7: "BLASST_E_ARG",
-    8: "BLASST_E_HIP",
+    8: "BLASST_E_HIP", 9: "BLASST_E_WORKSPACE",
 }
 
 # Every symbol include/blasst.h declares.
-EXPORTED = ("blasst_attn_prefill", "blasst_attn_decode", "blasst_status_string",
-            "blasst_last_error", "blasst_version")
+EXPORTED = ("blasst_attn_prefill", "blasst_attn_decode", "blasst_decode_workspace_size",
+            "blasst_status_string", "blasst_last_error", "blasst_version")
 
 
 class Shape(ctypes.Structure):
@@ -73,7 +73,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.blasst_attn_decode.restype = ctypes.c_int
     lib.blasst_attn_decode.argtypes = [vp, vp, vp, vp, u8p, fp, i64p, ctypes.POINTER(Shape),
                                        ctypes.c_int, ctypes.c_int, ctypes.c_float,
-                                       ctypes.c_float, ctypes.c_int, vp]
+                                       ctypes.c_float, ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.blasst_decode_workspace_size.restype = ctypes.c_int
+    lib.blasst_decode_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int,
+                                                 ctypes.POINTER(ctypes.c_size_t)]
     lib.blasst_status_string.restype = ctypes.c_char_p
     lib.blasst_status_string.argtypes = [ctypes.c_int]
     lib.blasst_last_error.restype = ctypes.c_char_p
@@ -168,10 +172,12 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: float, causa
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], lam: float,
            bc: int = 64, scale: Optional[float] = None, dv: Optional[int] = None,
            out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
-           want_mask: bool = True, want_lse: bool = True,
-           want_stats: bool = True) -> AttnResult:
+           want_mask: bool = True, want_lse: bool = True, want_stats: bool = True,
+           workspace: Optional[torch.Tensor] = None) -> AttnResult:
     """Skip-softmax decode. q [B,Hq,d]; k_cache [B,Hkv,Nk,d]; v_cache [B,Hkv,Nk,dv] or
-    None for a latent cache whose values are k_cache[..., :dv]."""
+    None for a latent cache whose values are k_cache[..., :dv]. `workspace` is a
+    uint8 device tensor of at least decode_workspace_size(...) bytes; when None
+    one is allocated through torch's caching allocator."""
     lib = load_library()
     _require_device(q, k_cache, v_cache, out)
     B, Hq, d = q.shape
@@ -189,16 +195,48 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tenso
     stats = torch.empty((B, Hq, 3), dtype=torch.int64, device=dev) if want_stats else None
     vs = _strides3(v_cache) if v_cache is not None else (0, 0, 0)
     sh = Shape(B, Hq, Hkv, 1, Nk, d, dv, _strides3(q), _strides3(k_cache), vs, _strides3(out))
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.blasst_decode_workspace_size(ctypes.byref(sh), _dtype_code(q.dtype),
+                                            int(v_cache is not None), int(bc),
+                                            ctypes.byref(nbytes)))
+    if workspace is None and nbytes.value > 0:
+        workspace = _workspace(nbytes.value, dev)
+    if workspace is not None:
+        _require_device(workspace)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = lib.blasst_attn_decode(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(mask),
                                 _ptr(lse), _ptr(stats), ctypes.byref(sh), _dtype_code(q.dtype),
-                                _dtype_code(out.dtype), float(lam), float(scale) if scale else 0.0, int(bc), _stream(dev))
+                                _dtype_code(out.dtype), float(lam),
+                                float(scale) if scale else 0.0, int(bc), _ptr(workspace),
+                                ws_bytes, _stream(dev))
     _check(st)
     return AttnResult(out, mask, lse, stats)
+
+
+def decode_workspace_size(B: int, Hq: int, Hkv: int, Nk: int, d: int, dv: int,
+                          latent: bool, dtype: torch.dtype = torch.bfloat16,
+                          bc: int = 64) -> int:
+    """Bytes of device workspace blasst_attn_decode needs (0 if none)."""
+    lib = load_library()
+    z = (0, 0, 0)
+    sh = Shape(B, Hq, Hkv, 1, Nk, d, dv, z, z, z, z)
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.blasst_decode_workspace_size(ctypes.byref(sh), _dtype_code(dtype),
+                                            int(not latent), int(bc), ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def _workspace(nbytes: int, dev: torch.device) -> torch.Tensor:
+    # torch's caching allocator hands out 512-byte aligned blocks; the library
+    # needs 256
+    t = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    assert t.data_ptr() % 256 == 0
+    return t
 
 
 def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
-__all__ = ["prefill", "decode", "load_library", "Shape", "BlasstError", "AttnResult",
+__all__ = ["prefill", "decode", "decode_workspace_size", "load_library", "Shape", "BlasstError", "AttnResult",
            "EXPORTED", "LIB_PATH", "STATUS"]

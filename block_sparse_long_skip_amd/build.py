@@ -24,6 +24,11 @@ LIB = os.path.join(HERE, "libblasst.so")
 SOURCES = ["api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "decode.hip", "decode_mla.hip"]
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
+# Per-source device flags. The latent-cache decode kernel keeps its output
+# accumulators in VGPRs (MFMA VGPR form) because it rescales them on the VALU
+# every time a running max grows; with the default AGPR form the compiler
+# copies all of them between register files at every loop iteration.
+SOURCE_FLAGS = {"decode_mla.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall",
           "-Wno-unused-function", f"-I{os.path.join(ROOT, 'include')}"]
 
@@ -37,7 +42,8 @@ def hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS
+    cmd = ([hipcc(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj] + COMMON + DEVICE_FLAGS
+           + SOURCE_FLAGS.get(src, []))
     r = subprocess.run(cmd, capture_output=True, text=True)
     # the host pass does not know the packed-fp32 target feature; that warning is expected
     noise = "is not a recognized feature for this target"

@@ -17,7 +17,8 @@ namespace blasst {
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t stream);
-hipError_t launch_decode_mla(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_mla(const DecodeArgs& a, void* workspace, hipStream_t stream);
+size_t decode_mla_workspace_bytes(int B, int Hq, int Hkv, int G, int nkt);
 
 __global__ void zero_i64_kernel(int64_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -106,6 +107,7 @@ const char* blasst_status_string(blasst_status_t s) {
     case BLASST_E_UNSUPPORTED: return "BLASST_E_UNSUPPORTED: no kernel for this combination";
     case BLASST_E_ARG: return "BLASST_E_ARG: invalid scalar argument";
     case BLASST_E_HIP: return "BLASST_E_HIP: HIP runtime error";
+    case BLASST_E_WORKSPACE: return "BLASST_E_WORKSPACE: workspace missing, too small or misaligned";
   }
   return "BLASST: unknown status";
 }
@@ -179,17 +181,15 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
   return hip_status(e, "prefill launch");
 }
 
-blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const void* v_cache,
-                                   void* out, uint8_t* mask_out, float* lse_out,
-                                   int64_t* stats_out, const blasst_shape_t* shape,
-                                   blasst_dtype_t dtype, blasst_dtype_t out_dtype, float lambda,
-                                   float scale, int bc, void* stream) {
-  blasst_status_t st0;
-  if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
-  if (!q || !k_cache || !out) return fail(BLASST_E_NULL, "q, k_cache and out are required");
-  st0 = check_dtypes(dtype, out_dtype);
-  if (st0 != BLASST_OK) return st0;
-  const blasst_shape_t& s = *shape;
+}  // extern "C"
+
+namespace {
+
+enum class DecodeKernel { kGqa, kLatent };
+
+// Validation shared by the decode entry point and its workspace query.
+blasst_status_t check_decode(const blasst_shape_t& s, blasst_dtype_t dtype, bool has_v, int bc,
+                             DecodeKernel* kind) {
   if (s.batch < 0 || s.heads_q < 1 || s.heads_kv < 1 || s.len_kv < 1 || s.d_qk < 1 || s.d_v < 1)
     return fail(BLASST_E_SHAPE, "sizes out of range (B=%d Hq=%d Hkv=%d Nk=%d d=%d dv=%d)",
                 s.batch, s.heads_q, s.heads_kv, s.len_kv, s.d_qk, s.d_v);
@@ -197,10 +197,60 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
   if (s.heads_q % s.heads_kv != 0)
     return fail(BLASST_E_SHAPE, "heads_q (%d) must be a multiple of heads_kv (%d)", s.heads_q,
                 s.heads_kv);
-  if (!v_cache && s.d_v >= s.d_qk)
+  if (!has_v && s.d_v >= s.d_qk)
     return fail(BLASST_E_SHAPE, "a latent cache (v_cache NULL) needs d_v < d_qk");
   if (bc < 1) return fail(BLASST_E_SHAPE, "tile size must be positive");
-  blasst_status_t st = check_lambda_scale(lambda, scale);
+  const int G = s.heads_q / s.heads_kv;
+  const bool gqa = dtype == BLASST_BF16 && has_v && s.d_qk == 128 && s.d_v == 128 && bc == 64 &&
+                   G <= 16;
+  const bool mla = dtype == BLASST_BF16 && !has_v && s.d_qk == 576 && s.d_v == 512 && bc == 64;
+  if (!gqa && !mla)
+    return fail(BLASST_E_UNSUPPORTED,
+                "no decode kernel for dtype=%d d_qk=%d d_v=%d bc=%d G=%d v_cache=%s (supported: "
+                "bf16 128/128 bc=64 G<=16; bf16 latent 576/512 bc=64)",
+                (int)dtype, s.d_qk, s.d_v, bc, G, has_v ? "set" : "NULL");
+  *kind = gqa ? DecodeKernel::kGqa : DecodeKernel::kLatent;
+  return BLASST_OK;
+}
+
+size_t decode_workspace(const blasst_shape_t& s, DecodeKernel kind, int bc) {
+  if (kind == DecodeKernel::kGqa || s.batch == 0) return 0;
+  const int nkt = (s.len_kv + bc - 1) / bc;
+  return blasst::decode_mla_workspace_bytes(s.batch, s.heads_q, s.heads_kv,
+                                            s.heads_q / s.heads_kv, nkt);
+}
+
+}  // namespace
+
+extern "C" {
+
+blasst_status_t blasst_decode_workspace_size(const blasst_shape_t* shape, blasst_dtype_t dtype,
+                                             int has_v_cache, int bc, size_t* bytes) {
+  if (!shape || !bytes) return fail(BLASST_E_NULL, "shape and bytes are required");
+  blasst_status_t st = check_dtypes(dtype, dtype);
+  if (st != BLASST_OK) return st;
+  DecodeKernel kind;
+  st = check_decode(*shape, dtype, has_v_cache != 0, bc, &kind);
+  if (st != BLASST_OK) return st;
+  *bytes = decode_workspace(*shape, kind, bc);
+  return ok();
+}
+
+blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                                   void* out, uint8_t* mask_out, float* lse_out,
+                                   int64_t* stats_out, const blasst_shape_t* shape,
+                                   blasst_dtype_t dtype, blasst_dtype_t out_dtype, float lambda,
+                                   float scale, int bc, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
+  if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
+  if (!q || !k_cache || !out) return fail(BLASST_E_NULL, "q, k_cache and out are required");
+  blasst_status_t st = check_dtypes(dtype, out_dtype);
+  if (st != BLASST_OK) return st;
+  const blasst_shape_t& s = *shape;
+  DecodeKernel kind;
+  st = check_decode(s, dtype, v_cache != nullptr, bc, &kind);
+  if (st != BLASST_OK) return st;
+  st = check_lambda_scale(lambda, scale);
   if (st != BLASST_OK) return st;
   const int elem = dtype == BLASST_FP32 ? 4 : 2;
   const int oelem = out_dtype == BLASST_FP32 ? 4 : 2;
@@ -209,24 +259,24 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
   if (!strides_aligned(s.q_stride, 2, elem) || !strides_aligned(s.k_stride, 3, elem) ||
       (v_cache && !strides_aligned(s.v_stride, 3, elem)) || !strides_aligned(s.o_stride, 2, oelem))
     return fail(BLASST_E_ALIGN, "every stride times the element size must be a multiple of 16");
-  const int G = s.heads_q / s.heads_kv;
-  const bool gqa = dtype == BLASST_BF16 && v_cache && s.d_qk == 128 && s.d_v == 128 && bc == 64 &&
-                   G <= 16;
-  const bool mla = dtype == BLASST_BF16 && !v_cache && s.d_qk == 576 && s.d_v == 512 && bc == 64;
-  if (!gqa && !mla)
-    return fail(BLASST_E_UNSUPPORTED,
-                "no decode kernel for dtype=%d d_qk=%d d_v=%d bc=%d G=%d v_cache=%s (supported: "
-                "bf16 128/128 bc=64 G<=16; bf16 latent 576/512 bc=64)",
-                (int)dtype, s.d_qk, s.d_v, bc, G, v_cache ? "set" : "NULL");
-  if (mla && stats_out && !mask_out)
-    return fail(BLASST_E_NULL, "stats_out for a latent cache needs mask_out (the V-tile count "
-                               "spans several workgroups and is taken from the mask)");
+  if (kind == DecodeKernel::kLatent && s.k_stride[2] * 2 * 64 > (int64_t)UINT32_MAX)
+    return fail(BLASST_E_UNSUPPORTED, "latent cache row stride too large (%lld elements)",
+                (long long)s.k_stride[2]);
+  const size_t need = decode_workspace(s, kind, bc);
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need)
+      return fail(BLASST_E_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need,
+                  workspace ? workspace_bytes : (size_t)0, workspace);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(BLASST_E_WORKSPACE, "workspace must be 256-byte aligned");
+  }
 
   const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)s.d_qk));
   blasst::DecodeArgs a;
   a.q = q; a.k = k_cache; a.v = v_cache; a.out = out;
   a.mask = mask_out; a.lse = lse_out; a.stats = stats_out;
-  a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nk = s.len_kv; a.G = G;
+  a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nk = s.len_kv;
+  a.G = s.heads_q / s.heads_kv;
   a.nkt = (s.len_kv + bc - 1) / bc;
   a.out_f32 = out_dtype == BLASST_FP32 ? 1 : 0;
   a.qs0 = s.q_stride[0]; a.qs1 = s.q_stride[1];
@@ -239,7 +289,8 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
 
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   if (s.batch == 0) return ok();
-  const hipError_t e = gqa ? blasst::launch_decode_gqa(a, hs) : blasst::launch_decode_mla(a, hs);
+  const hipError_t e = kind == DecodeKernel::kGqa ? blasst::launch_decode_gqa(a, hs)
+                                                  : blasst::launch_decode_mla(a, workspace, hs);
   return hip_status(e, "decode launch");
 }
 

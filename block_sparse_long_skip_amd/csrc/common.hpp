@@ -124,6 +124,27 @@ __device__ __forceinline__ void store16(void* p, const u32x4_t& v) {
   *reinterpret_cast<u32x4_t*>(p) = v;
 }
 
+typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
+
+// gfx950 transposing LDS read (ds_read_b64_tr_b16): within each group of 16
+// lanes, lane i receives element i%4 of the 4-element rows addressed by lanes
+// i/4, 4 + i/4, 8 + i/4 and 12 + i/4.
+__device__ __forceinline__ u32x2_t ds_read_tr(const char* p) {
+  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                         (__attribute__((address_space(3))) s16x4_t*)(p)));
+}
+
+// global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4): lane l's
+// bytes land at lds_base + 16 l; lds_base must be the same in every lane.
+__device__ __forceinline__ void lds_dma16(const void* src, char* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   0);
+}
+
+// wait for this wave's outstanding global memory operations, including the
+// copies into LDS
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 __global__ void zero_i64_kernel(int64_t* p, int64_t n);
 
 }  // namespace blasst

@@ -36,15 +36,10 @@ constexpr int NW = 4;
 constexpr int NT = NW * 64;
 constexpr int SLICE = BC * D * 2;  // 16 KB: one V tile, 64 rows x 256 B
 
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
 
 // 16-byte chunk c of row r of a 64 x 256 B tile, chunk index XOR-swizzled by the row
 __device__ __forceinline__ int vswz(int r, int c) {
   return r * 256 + ((c ^ (((r & 3) << 2) | ((r >> 2) & 3))) << 4);
-}
-__device__ __forceinline__ u32x2_t ds_read_tr(const char* p) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                         (__attribute__((address_space(3))) s16x4_t*)(p)));
 }
 }  // namespace
 

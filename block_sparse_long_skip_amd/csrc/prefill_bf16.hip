@@ -58,25 +58,10 @@ constexpr int NT = 256;
 constexpr int TILE_BYTES = BC * D * 2;  // 16 KB
 constexpr float kLazyRescaleLog2 = 8.f;  // rescale once the max grows by 2^8
 
-typedef __attribute__((__vector_size__(4 * sizeof(short)))) short s16x4_t;
-
 // XOR applied to the 16-byte chunk index of tile row `row`
 __device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
 // byte offset of (row, 16-byte chunk c) inside a 64 x 256 B tile
 __device__ __forceinline__ int swz(int row, int c) { return row * 256 + ((c ^ swz_f(row)) << 4); }
-
-__device__ __forceinline__ u32x2_t ds_read_tr(const char* p) {
-  return __builtin_bit_cast(u32x2_t, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                         (__attribute__((address_space(3))) s16x4_t*)(p)));
-}
-
-__device__ __forceinline__ void lds_dma16(const void* src, char* lds_row_base) {
-  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_row_base, 16,
-                                   0, 0);
-}
-
-// wait for this wave's outstanding global loads (including the ones into LDS)
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 struct RowState {
   float m_prefix;  // exact running max (raw q.k units) of this lane's row, -inf before tile 0

@@ -29,7 +29,8 @@
  *
  * Conventions shared by every entry point:
  *   - Every tensor pointer is a DEVICE pointer owned by the caller. The library
- *     allocates no memory and keeps no per-call state; calls are reentrant.
+ *     allocates no memory and keeps no per-call state; calls are reentrant as
+ *     long as concurrent calls do not share a decode workspace.
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the legacy
  *     default stream). Outputs are valid once the stream has synchronised.
  *   - All arguments are validated before any HIP call. On any error nothing is
@@ -56,7 +57,7 @@
 extern "C" {
 #endif
 
-#define BLASST_VERSION 100 /* 1.0.0 */
+#define BLASST_VERSION 200 /* 2.0.0: decode takes a workspace */
 
 typedef enum blasst_status {
   BLASST_OK = 0,
@@ -68,7 +69,10 @@ typedef enum blasst_status {
   BLASST_E_ALIGN = 5,       /* pointer or stride not 16-byte aligned */
   BLASST_E_UNSUPPORTED = 6, /* valid request with no kernel in this build */
   BLASST_E_ARG = 7,         /* other bad scalar argument (non-finite scale) */
-  BLASST_E_HIP = 8          /* a HIP runtime call failed */
+  BLASST_E_HIP = 8,         /* a HIP runtime call failed */
+  BLASST_E_WORKSPACE = 9    /* decode workspace NULL, smaller than
+                               blasst_decode_workspace_size() or not 256-byte
+                               aligned */
 } blasst_status_t;
 
 typedef enum blasst_dtype {
@@ -145,19 +149,35 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
  *   stats_out nullable, contiguous int64 [B, Hq, 3]: {visited key tiles, kept
  *             key tiles, V tiles read for this head's KV head}. A V tile is
  *             read when any query head sharing the KV head keeps it.
+ *   workspace device memory of at least blasst_decode_workspace_size() bytes,
+ *             256-byte aligned, owned by the caller; contents on entry are
+ *             ignored and on return are undefined. May be NULL when that size
+ *             is 0. Calls that overlap in time must not share a workspace.
  *
  * Supported (else BLASST_E_UNSUPPORTED), all BLASST_BF16 inputs with bc = 64:
  *   d_qk = d_v = 128 with a separate v_cache, heads_q / heads_kv <= 16
- *   d_qk = 576, d_v = 512, v_cache NULL (latent cache), any heads_q / heads_kv
- *   (the query heads of a KV head are processed in groups of 16). For a
- *   latent cache, stats_out requires mask_out: the V-tile count spans the
- *   workgroups of several head groups and is taken from the mask.
+ *           (no workspace);
+ *   d_qk = 576, d_v = 512, v_cache NULL (latent cache), any heads_q / heads_kv.
+ *           The cache is split along its length over workgroups; the
+ *           workspace holds the tile maxima, the per-split partial outputs
+ *           and their log-sum-exp statistics, merged at the end. It grows
+ *           with B * Hq * (ceil(Nk/64) + 2 KB per split).
  */
 blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const void* v_cache,
                                    void* out, uint8_t* mask_out, float* lse_out,
                                    int64_t* stats_out, const blasst_shape_t* shape,
                                    blasst_dtype_t dtype, blasst_dtype_t out_dtype, float lambda,
-                                   float scale, int bc, void* stream);
+                                   float scale, int bc, void* workspace, size_t workspace_bytes,
+                                   void* stream);
+
+/*
+ * Workspace bytes blasst_attn_decode needs for this shape, dtype, cache kind
+ * (has_v_cache = 0 for a latent cache) and tile size; 0 when none is needed.
+ * Validates like blasst_attn_decode (sizes, dtype, supported combination) and
+ * writes *bytes only on BLASST_OK. Launches nothing.
+ */
+blasst_status_t blasst_decode_workspace_size(const blasst_shape_t* shape, blasst_dtype_t dtype,
+                                             int has_v_cache, int bc, size_t* bytes);
 
 /* Static text for a status code. */
 const char* blasst_status_string(blasst_status_t status);

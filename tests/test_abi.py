@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(A.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.blasst_version() == 100
+    assert lib.blasst_version() == 200
 
 
 def test_status_strings():
@@ -60,10 +60,18 @@ def _prefill(sh, q=P, k=P, v=P, out=P, dtype=BF16, lam=1e-3, scale=0.0, causal=1
 
 
 def _decode(sh, q=P, k=P, v=P, out=P, mask=None, stats=None, dtype=BF16, lam=1e-3, bc=64,
-            out_dtype=None):
+            out_dtype=None, ws=None, ws_bytes=0):
     lib = A.load_library()
     return lib.blasst_attn_decode(q, k, v, out, mask, None, stats, ctypes.byref(sh), dtype,
-                                  dtype if out_dtype is None else out_dtype, lam, 0.0, bc, None)
+                                  dtype if out_dtype is None else out_dtype, lam, 0.0, bc, ws,
+                                  ws_bytes, None)
+
+
+def _ws_size(sh, has_v, dtype=BF16, bc=64):
+    n = ctypes.c_size_t(12345)
+    st = A.load_library().blasst_decode_workspace_size(ctypes.byref(sh), dtype, int(has_v), bc,
+                                                        ctypes.byref(n))
+    return st, n.value
 
 
 def _err():
@@ -125,7 +133,8 @@ def test_prefill_validation(case, expect):
 
 @pytest.mark.parametrize("case,expect", [
     ("len_q", 2), ("latent_dv", 2), ("gqa_too_many_heads", 6), ("bad_bc", 6),
-    ("mla_stats_without_mask", 1), ("null_k", 1), ("lam", 4), ("f32", 6),
+    ("null_k", 1), ("lam", 4), ("f32", 6), ("mla_no_workspace", 9),
+    ("mla_small_workspace", 9), ("mla_misaligned_workspace", 9),
 ])
 def test_decode_validation(case, expect):
     sh = _shape(Hq=8, Hkv=2, Nq=1, Nk=1000)
@@ -139,9 +148,14 @@ def test_decode_validation(case, expect):
         sh.heads_q, sh.heads_kv = 64, 2
     elif case == "bad_bc":
         kw["bc"] = 128
-    elif case == "mla_stats_without_mask":
+    elif case.startswith("mla_"):
         sh = _shape(Hq=32, Hkv=1, Nq=1, Nk=1000, d=576, dv=512)
-        kw["v"], kw["stats"] = None, P
+        kw["v"], kw["stats"], kw["mask"] = None, P, P
+        need = _ws_size(sh, False)[1]
+        if case == "mla_small_workspace":
+            kw["ws"], kw["ws_bytes"] = P, need - 1
+        elif case == "mla_misaligned_workspace":
+            kw["ws"], kw["ws_bytes"] = P + 16, need
     elif case == "null_k":
         kw["k"] = None
     elif case == "lam":
@@ -149,6 +163,28 @@ def test_decode_validation(case, expect):
     elif case == "f32":
         kw["dtype"] = FP32
     assert _decode(sh, **kw) == expect, _err()
+
+
+def test_decode_workspace_size():
+    """GQA decode needs no workspace; a latent cache needs one that grows with
+    the cache length and the batch, and the query validates like the call."""
+    st, n = _ws_size(_shape(Hq=8, Hkv=2, Nq=1, Nk=1000), True)
+    assert (st, n) == (0, 0)
+    sizes = []
+    for B, Nk in [(1, 1000), (1, 64000), (4, 64000)]:
+        st, n = _ws_size(_shape(B=B, Hq=128, Hkv=1, Nq=1, Nk=Nk, d=576, dv=512), False)
+        assert st == 0 and n > 0 and n % 256 == 0, _err()
+        # at least the tile maxima and one partial output row per (batch, head)
+        assert n >= B * 128 * (4 * -(-Nk // 64) + 4 * 512)
+        sizes.append(n)
+    assert sizes[0] < sizes[1] < sizes[2]
+    st, _ = _ws_size(_shape(B=0, Hq=128, Hkv=1, Nq=1, Nk=64, d=576, dv=512), False)
+    assert st == 0
+    assert _ws_size(_shape(Hq=8, Hkv=2, Nq=2, Nk=1000), True)[0] == 2
+    assert _ws_size(_shape(Hq=8, Hkv=2, Nq=1, Nk=1000, d=96, dv=96), True)[0] == 6
+    lib = A.load_library()
+    sh = _shape(Hq=8, Hkv=2, Nq=1, Nk=1000)
+    assert lib.blasst_decode_workspace_size(ctypes.byref(sh), BF16, 1, 64, None) == 1
 
 
 def test_binding_has_no_cpu_fallback():

@@ -41,10 +41,10 @@ def _prefill(inp, w, lam, out="native", **kw):
     return r
 
 
-def _decode(inp, w, lam, out="native"):
+def _decode(inp, w, lam, out="native", workspace=None):
     q, k = to_device(inp.q, w), to_device(inp.k, w)
     v = to_device(inp.v, w) if inp.v is not None else None
-    r = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv, out_dtype=OUT.get(out))
+    r = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv, out_dtype=OUT.get(out), workspace=workspace)
     torch.cuda.synchronize()
     return r
 
@@ -199,12 +199,19 @@ def test_decode_gqa_b32_n65536(lam, gain, out):
         assert res.skip_fraction > 0.3
 
 
+# The latent-cache kernel splits the cache over workgroups (one split per
+# tile at these sizes, a few tiles per split at the larger ones) and redoes the
+# splits whose speculative decisions differ from the exact ones; two head
+# groups (G = 128), a partial group (G = 100) and several KV heads are covered.
 @pytest.mark.parametrize("shape", [
     dict(B=2, Hq=32, Hkv=1, Nk=1000),
     dict(B=1, Hq=20, Hkv=2, Nk=300),
     dict(B=1, Hq=16, Hkv=1, Nk=64),
+    dict(B=1, Hq=128, Hkv=1, Nk=2000),
+    dict(B=1, Hq=100, Hkv=1, Nk=5000),
+    dict(B=3, Hq=128, Hkv=2, Nk=9000),
 ])
-@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-2, 6.0)])
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 6.0), (1e-2, 6.0), (1.0, 6.0)])
 @pytest.mark.parametrize("out", ["bf16", "fp32"])
 def test_decode_mla_small(shape, lam, gain, out):
     w = synth.small_workload("decode_mla", d=576, dv=512, dtype="bf16", bc=64, gain=gain,
@@ -217,6 +224,25 @@ def test_decode_mla_small(shape, lam, gain, out):
 def test_decode_mla_b16_n32768(lam, gain, out):
     w = synth.WORKLOADS[5].with_gain(gain)
     _check_decode(w, lam, pairs=[(0, 0), (15, 0)], out=out)
+
+
+def test_decode_mla_workspace_reuse():
+    """The workspace carries nothing between calls: a call after another shape
+    has used (and left garbage in) the same buffer gives the same bits."""
+    w1 = synth.small_workload("decode_mla", d=576, dv=512, dtype="bf16", bc=64, gain=6.0,
+                              seed=56, window=64, B=2, Hq=64, Hkv=1, Nk=3000)
+    w2 = synth.small_workload("decode_mla", d=576, dv=512, dtype="bf16", bc=64, gain=1.0,
+                              seed=57, window=64, B=1, Hq=128, Hkv=1, Nk=5000)
+    n = max(A.decode_workspace_size(w.B, w.Hq, w.Hkv, w.Nk, 576, 512, latent=True)
+            for w in (w1, w2))
+    ws = torch.full((n,), 0xA5, dtype=torch.uint8, device="cuda")
+    i1, i2 = synth.make_inputs(w1), synth.make_inputs(w2)
+    r1 = _decode(i1, w1, 1e-2, "fp32", workspace=ws)
+    first = [x.clone() for x in (r1.out, r1.mask, r1.lse, r1.stats)]
+    _decode(i2, w2, 1e-3, "fp32", workspace=ws)
+    r3 = _decode(i1, w1, 1e-2, "fp32", workspace=ws)
+    for a_, b_ in zip(first, (r3.out, r3.mask, r3.lse, r3.stats)):
+        assert torch.equal(a_, b_)
 
 
 # ----------------------------------------------------------------------------- behaviour

@@ -259,7 +259,10 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
   if (!strides_aligned(s.q_stride, 2, elem) || !strides_aligned(s.k_stride, 3, elem) ||
       (v_cache && !strides_aligned(s.v_stride, 3, elem)) || !strides_aligned(s.o_stride, 2, oelem))
     return fail(BLASST_E_ALIGN, "every stride times the element size must be a multiple of 16");
-  if (kind == DecodeKernel::kLatent && s.k_stride[2] * 2 * 64 > (int64_t)UINT32_MAX)
+  if (kind == DecodeKernel::kLatent && s.k_stride[2] < s.d_qk)
+    return fail(BLASST_E_SHAPE, "latent cache rows overlap (k_stride[2] = %lld < d_qk = %d)",
+                (long long)s.k_stride[2], s.d_qk);
+  if (kind == DecodeKernel::kLatent && s.k_stride[2] * 2 * 64 > (int64_t)INT32_MAX)
     return fail(BLASST_E_UNSUPPORTED, "latent cache row stride too large (%lld elements)",
                 (long long)s.k_stride[2]);
   const size_t need = decode_workspace(s, kind, bc);

@@ -47,6 +47,7 @@
 //     128w..128w+127 of all 64 heads: O^T += V^T P^T, with V^T read from the
 //     key tile by ds_read_b64_tr_b16.
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 
@@ -59,22 +60,32 @@ constexpr int DV = 512;
 constexpr int NW = 4;
 constexpr int NT = NW * 64;
 constexpr int HG = 64;                    // query heads per workgroup
-constexpr int KS = DQK / 32;              // 18 MFMA steps over the key features
+constexpr int KS2 = DQK / 16;             // 36 MFMA steps (32x32x16) over the key features
 constexpr int ROWB = DQK * 2;             // 1152 bytes per key row
 constexpr int TILEB = BC * ROWB;          // 73728 bytes per tile
 constexpr int NCH = TILEB / 16;           // 4608 16-byte chunks per tile
 constexpr int DMA_PER_WAVE = NCH / 64 / NW;  // 18 copy instructions per wave per tile
 constexpr int PP = BC + 8;                // P^T row pitch (bf16): 144 B
-constexpr int LIST_MAX = 512;             // most tiles per split
+constexpr int LIST_MAX = 256;             // most tiles per split
 constexpr int TARGET_BLOCKS = 256;        // one workgroup per CU
+constexpr float kLazyRescaleLog2 = 8.f;   // rescale once the max grows by 2^8
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format, raw access
 static_assert(NCH % (64 * NW) == 0, "tile copies split evenly over the waves");
 static_assert(DV == 128 * NW, "each wave produces 128 output features");
 
-// XOR on the low 3 bits of the 16-byte chunk index of key row r: 8 distinct
+// LDS layout of a 64 x 576 key tile: 1 KB blocks of 8 rows x 8 chunks of 16
+// bytes, block (row / 8, chunk / 8) at 1024 * ((row / 8) * 9 + chunk / 8),
+// 128 bytes per row inside a block. One global_load_lds_dwordx4 fills one
+// block, so each lane's source offset inside a block is the same for every
+// copy. The chunk index inside a block is XOR-ed with mla_f(row): 8 distinct
 // values over the even rows (and over the odd rows) of any 16 consecutive
-// rows, and different high bits for rows r and r+2
+// rows, and a different bit 1 for rows r and r + 2, so the score operand reads
+// (16 rows, one chunk) and the transposing value reads (4 rows, 2 chunks) hit
+// distinct banks.
 __device__ __forceinline__ int mla_f(int r) { return (((r >> 1) & 3) << 1) | ((r >> 3) & 1); }
-__device__ __forceinline__ int mla_off(int r, int c) { return r * ROWB + ((c ^ mla_f(r)) << 4); }
+__device__ __forceinline__ int mla_off(int r, int c) {
+  return (((r >> 3) * (DQK / 64) + (c >> 3)) << 10) + ((r & 7) << 7) + (((c & 7) ^ mla_f(r)) << 4);
+}
 
 // Workgroup barrier for LDS data only: waits for this wave's LDS operations
 // but not for its copies into the other tile buffer, which stay in flight
@@ -82,6 +93,20 @@ __device__ __forceinline__ int mla_off(int r, int c) { return r * ROWB + ((c ^ m
 // the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One block row of a tile into LDS: block cb of the row comes from 128 cb
+// bytes further along the key rows. That offset goes in the scalar offset of
+// the buffer load: the immediate offset would move the LDS destination too.
+template <int CB>
+__device__ __forceinline__ void copy_block(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(
+      rs, (__attribute__((address_space(3))) void*)(lds + 1024 * CB), 16, voff, 128 * CB, 0, 0);
+}
+template <int... CB>
+__device__ __forceinline__ void copy_block_row(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff,
+                                               std::integer_sequence<int, CB...>) {
+  (copy_block<CB>(rs, lds, voff), ...);
 }
 
 // gap of a tile max against a running max, with the conventions of the drop
@@ -95,9 +120,11 @@ __device__ __forceinline__ float gap_of(float tm, float m) {
 
 // Workspace of one latent-cache decode call (carved from the caller's buffer).
 struct MlaWork {
-  float* tmax;     // [B*Hq][nkt]           tile maxima (raw q.k units)
+  float* tmax;     // [B*Hkv][nkt][G]       tile maxima (raw q.k units), heads fastest
+  float* smax;     // [B*Hq][nsplit]        maximum of each split's tile maxima
   float* part_o;   // [B*Hq][nsplit][512]   unnormalised partial outputs
-  float* part_ml;  // [B*Hq][nsplit][2]     partial (running max, row sum)
+  float* part_ml;  // [B*Hq][nsplit][4]     partial (reference max, row sum, row sum of the
+                   //                       bf16-rounded p, unused)
   int* part_kept;  // [B*Hq][nsplit]        kept tiles per split (exact decisions)
   uint8_t* anyk;   // [B*Hkv][ngroups][nkt] 1 if some head of the group keeps the tile
   int ngroups, nsplit, T;
@@ -112,16 +139,19 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
   __shared__ __attribute__((aligned(16))) uint16_t Ps[HG * PP];
   __shared__ float tmw[2][2][HG];  // [buffer][key half][head]
   __shared__ float alph[HG];
-  __shared__ float lred[2][HG];
+  __shared__ float lred[2][2][HG];  // [sum kind][key half][head]
   __shared__ int kflag[NW];
   __shared__ uint16_t list[LIST_MAX];  // kept tiles of the split, relative to its first
+  __shared__ float mstart[HG];         // exact running max entering the split
+  __shared__ int cntw[NW][HG];
+  __shared__ int misw[NW];
   __shared__ int nlist;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
-  const int n = lane & 15;
-  const int g = lane >> 4;
+  const int l32 = lane & 31;
+  const int h = lane >> 5;
   const int kh = w & 1, hh = w >> 1;
 
   // logical block = ((split * B*Hkv) + seq) * ngroups + group: the head groups
@@ -145,84 +175,90 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
   const int64_t row0 = (int64_t)b * a.Hq + kvh * G + h0;  // (b, head h0 of the group)
   const int nsplit = ws.nsplit;
   const int Nk = a.Nk;
-  float* const tmaxp = ws.tmax;
+  float* const tmaxp = ws.tmax + (int64_t)seq * nkt * G + h0;  // + j * G + head
 
-  // this lane's two score heads (head half hh, blocks hb = 0, 1)
-  int hl[2];
-  bool hv[2];
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    hl[hb] = 32 * hh + 16 * hb + n;
-    hv[hb] = h0 + hl[hb] < G;
-  }
+  // the score head of this lane: S^T[32 keys][32 heads] per wave, head 32hh + l32
+  const int hl = 32 * hh + l32;
+  const bool hv = h0 + hl < G;
 
-  // ---- exact decisions (pass 1): true prefix max at the split, mask, counts
-  float m_init[2] = {kNegInf, kNegInf};
+  // ---- exact decisions (pass 1): true running max entering the split, mask,
+  // counts, and whether pass 0 took the same decisions
+  float m_init = kNegInf;
   int nl = j1 - j0;
   if constexpr (MODE == 1) {
-    float* pmw = reinterpret_cast<float*>(Ps);  // [NW][HG] maxima of the tiles before the split
-    float* smw = pmw + NW * HG;                 // [NW][HG] maxima of each wave's share of the split
-    int* cntw = reinterpret_cast<int*>(smw + NW * HG);  // [NW][HG]
-    int* misw = cntw + NW * HG;                         // [NW]
-    uint8_t* tflag = reinterpret_cast<uint8_t*>(misw + NW);  // [T]
-    const int h = lane;
-    const bool hvl = h0 + h < G;
-    const int64_t row = row0 + h;
-    const float* tr = ws.tmax + row * nkt;
-    float pmx = kNegInf;
-    if (hvl)
-      for (int j = (w * j0) / NW; j < ((w + 1) * j0) / NW; ++j) pmx = fmaxf(pmx, tr[j]);
     const int tn = j1 - j0;
-    const int q0 = j0 + (w * tn) / NW, q1 = j0 + ((w + 1) * tn) / NW;
-    float smx = kNegInf;
-    if (hvl)
-      for (int j = q0; j < q1; ++j) smx = fmaxf(smx, tr[j]);
-    pmw[w * HG + h] = pmx;
-    smw[w * HG + h] = smx;
-    __syncthreads();
-    // running maxima entering this wave's share: exact (from tile 0) and as
-    // pass 0 had them (from the split's first tile)
-    float mt = fmaxf(fmaxf(pmw[h], pmw[HG + h]), fmaxf(pmw[2 * HG + h], pmw[3 * HG + h]));
-    float ml = kNegInf;
-    for (int v = 0; v < w; ++v) {
-      mt = fmaxf(mt, smw[v * HG + h]);
-      ml = fmaxf(ml, smw[v * HG + h]);
+    float* tms = reinterpret_cast<float*>(Kt1);   // [tn][HG] tile maxima of the split
+    uint8_t* mk = reinterpret_cast<uint8_t*>(Kt0);  // [HG][LIST_MAX] exact decisions
+    uint8_t* tflag = mk + HG * LIST_MAX;             // [tn] some head keeps the tile
+    const int hp = lane;  // one head per lane
+    const bool hvp = h0 + hp < G;
+    // the split's tile maxima into LDS, 16 independent loads per wave at a time
+    for (int c = 0; c < tn; c += 16 * NW) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int jj = c + NW * u + w;
+        v[u] = (hvp && jj < tn) ? tmaxp[(int64_t)(j0 + jj) * G + hp] : kNegInf;
+      }
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        const int jj = c + NW * u + w;
+        if (jj < tn) tms[jj * HG + hp] = v[u];
+      }
     }
+    // maximum of the tile maxima before the split: the split maxima of pass 0
+    if (w == 0) {
+      float M = kNegInf;
+      if (hvp) {
+        const float* sm = ws.smax + (row0 + hp) * nsplit;
+#pragma unroll 8
+        for (int x = 0; x < s; ++x) M = fmaxf(M, sm[x]);
+      }
+      mstart[hp] = M;
+    }
+    __syncthreads();
+    // wave w takes a quarter of the split; the running maxima entering it
+    // follow from the tiles before it (a dropped tile's max is below the
+    // running max, so the plain max is the running max over kept tiles)
+    const int q0 = (w * tn) / NW, q1 = ((w + 1) * tn) / NW;
+    float ml = kNegInf;  // as pass 0 had it: from the split's first tile
+    for (int jj = 0; jj < q0; ++jj) ml = fmaxf(ml, tms[jj * HG + hp]);
+    float mt = fmaxf(mstart[hp], ml);  // exact: from tile 0
     int cnt = 0;
     bool mis = false;
-    uint8_t* anyrow = ws.anyk + ((int64_t)seq * ws.ngroups + gi) * nkt;
-    for (int j = q0; j < q1; ++j) {
-      const float tm = hvl ? tr[j] : kNegInf;
-      const bool kt = hvl && (j == 0 || !(gap_of(tm, mt) < thr));
-      const bool kl = hvl && (j == 0 || !(gap_of(tm, ml) < thr));
-      // a dropped tile's max is below the running max, so the plain max is
-      // the running max over kept tiles
+    uint8_t* anyrow = ws.anyk + ((int64_t)seq * ws.ngroups + gi) * nkt + j0;
+    for (int jj = q0; jj < q1; ++jj) {
+      const float tm = tms[jj * HG + hp];
+      const int j = j0 + jj;
+      const bool kt = hvp && (j == 0 || !(gap_of(tm, mt) < thr));
+      const bool kl = hvp && (j == 0 || !(gap_of(tm, ml) < thr));
       mt = fmaxf(mt, tm);
       ml = fmaxf(ml, tm);
       cnt += kt ? 1 : 0;
       mis |= kt != kl;
-      if (a.mask && hvl) a.mask[row * nkt + j] = kt ? 1 : 0;
+      mk[hp * LIST_MAX + jj] = kt ? 1 : 0;
       const bool any = __ballot(kt) != 0;
       if (lane == 0) {
-        tflag[j - j0] = any ? 1 : 0;
-        anyrow[j] = any ? 1 : 0;
+        tflag[jj] = any ? 1 : 0;
+        anyrow[jj] = any ? 1 : 0;
       }
     }
-    cntw[w * HG + h] = cnt;
+    cntw[w][hp] = cnt;
     const bool wmis = __ballot(mis) != 0;
     if (lane == 0) misw[w] = wmis ? 1 : 0;
     __syncthreads();
-    if (w == 0 && hvl)
-      ws.part_kept[row * nsplit + s] =
-          cntw[h] + cntw[HG + h] + cntw[2 * HG + h] + cntw[3 * HG + h];
-    const bool redo = (misw[0] | misw[1] | misw[2] | misw[3]) != 0;
-    if (!redo) return;  // the pass-0 partial is exact
-    // the score lanes start from the exact prefix max at the split
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const int x = hl[hb];
-      m_init[hb] = fmaxf(fmaxf(pmw[x], pmw[HG + x]), fmaxf(pmw[2 * HG + x], pmw[3 * HG + x]));
+    // mask rows of the group's heads, consecutive threads on consecutive tiles
+    if (a.mask) {
+      for (int idx = t; idx < HG * tn; idx += NT) {
+        const int hx = idx / tn, jj = idx - hx * tn;
+        if (h0 + hx < G) a.mask[(row0 + hx) * nkt + j0 + jj] = mk[hx * LIST_MAX + jj];
+      }
     }
+    if (w == 0 && hvp)
+      ws.part_kept[(row0 + hp) * nsplit + s] = cntw[0][hp] + cntw[1][hp] + cntw[2][hp] + cntw[3][hp];
+    const bool redo = (misw[0] | misw[1] | misw[2] | misw[3]) != 0;
+    if (!redo) return;  // the pass-0 partial is already exact
+    m_init = mstart[hl];
     // list of the tiles some head keeps, in order
     if (w == 0) {
       int base = 0;
@@ -234,89 +270,100 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
       }
       if (lane == 0) nlist = base;
     }
-    __syncthreads();
+    __syncthreads();  // list ready; mk and tms (in the tile buffers) no longer read
     nl = nlist;
   }
   auto tile_of = [&](int idx) __attribute__((always_inline)) -> int {
-    if constexpr (MODE == 1) return j0 + list[idx];
+    if constexpr (MODE == 1) return j0 + __builtin_amdgcn_readfirstlane((int)list[idx]);
     else return j0 + idx;
   };
 
-  // ---- queries: q^T as the B operand, lane supplies q[head hl][32kk + 8g .. +7]
-  bf16x8_t qb[2][KS];
+  // ---- queries: q^T as the B operand of v_mfma_f32_32x32x16_bf16, lane
+  // supplies q[head hl][16kk + 8h .. +7]; kept in AGPRs (MFMA operands may be AGPRs)
+  bf16x8_t qb[KS2];
+  {
+    const uint16_t* qp = (const uint16_t*)a.q + b * a.qs0 +
+                         (int64_t)(kvh * G + h0 + (hv ? hl : 0)) * a.qs1;
+    u32x4_t v[KS2];
 #pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    const uint16_t* qp = (const uint16_t*)a.q + b * a.qs0 + (int64_t)(kvh * G + h0 + hl[hb]) * a.qs1;
+    for (int kk = 0; kk < KS2; ++kk) v[kk] = load16(qp + 16 * kk + 8 * h);  // all in flight
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      u32x4_t v = {0u, 0u, 0u, 0u};
-      if (hv[hb]) v = load16(qp + 32 * kk + 8 * g);
-      asm volatile("" : "+a"(v));  // queries live in AGPRs (MFMA operands may be AGPRs)
-      qb[hb][kk] = as_bf16x8(v);
+    for (int kk = 0; kk < KS2; ++kk) {
+      u32x4_t x = hv ? v[kk] : (u32x4_t){0u, 0u, 0u, 0u};
+      asm volatile("" : "+a"(x));
+      qb[kk] = as_bf16x8(x);
     }
   }
 
   // ---- per-lane LDS offsets
-  // score operand (A = K rows): key row 32kh + 16kb + n, chunk 4kk + g; kk
-  // even/odd give two patterns, kk >> 1 adds 128 bytes, kb adds 16 rows
-  const int kr = 32 * kh + n;
-  const int ko_even = kr * ROWB + (((g ^ mla_f(kr)) & 7) << 4);
-  const int ko_odd = kr * ROWB + ((((4 + g) ^ mla_f(kr)) & 7) << 4);
-  // value operand (A = V^T, transposing read): lane group g reads keys
-  // 32cc + 8g + n/4 (and +4), features 128w + 16db + 4(n&3); cc adds 32 rows,
-  // db >> 2 adds 128 bytes
-  int vo[4][2];
+  // score operand (A = K rows): key row 32kh + l32, chunk 2kk + h; kk & 3
+  // selects one of four patterns and kk >> 2 the next block (1024 bytes)
+  const int kr = 32 * kh + l32;
+  int ko[4];
 #pragma unroll
-  for (int d4 = 0; d4 < 4; ++d4)
+  for (int x = 0; x < 4; ++x) ko[x] = mla_off(kr, 2 * x + h);
+  // value operand (A = V^T, transposing read), 16-key step ks: lane (group
+  // gq = lane/16, j = lane%16) reads key 16ks + 8(gq>>1) + 4hf + j/4 at
+  // features 128w + 32db + 16(gq&1) + 4(j&3); db & 1 selects one of two
+  // patterns, db >> 1 the next block, ks two block rows (18 KB)
+  const int gq = lane >> 4, jq = lane & 15;
+  int vo[2][2];
+#pragma unroll
+  for (int d1 = 0; d1 < 2; ++d1)
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
-      const int r = 8 * g + (n >> 2) + 4 * hf;
-      const int c = 16 * w + 2 * d4 + ((n & 3) >> 1);
-      vo[d4][hf] = mla_off(r, c) + ((n & 1) << 3);
+      const int r = 8 * (gq >> 1) + 4 * hf + (jq >> 2);
+      const int dv0 = 128 * w + 32 * d1 + 16 * (gq & 1) + 4 * (jq & 3);
+      vo[d1][hf] = mla_off(r, dv0 >> 3) + ((dv0 & 7) << 1);
     }
 
-  // ---- tile copies: wave w issues copies 18w..18w+17; copy q fills LDS chunks
-  // 64q..64q+63, lane l chunk p = 64q + l = (row p / 72, physical chunk p % 72),
-  // so it fetches the logical chunk the swizzle maps there
+  // ---- tile copies: wave w fills blocks 18w..18w+17 of a tile (block rows
+  // 2w and 2w + 1); in block (rb, cb) lane l lands at row 8rb + l/8, physical
+  // chunk l%8, so it fetches logical chunk 8cb + ((l%8) ^ mla_f(row)). That
+  // offset depends on the lane and on rb & 1 only; the block's own offset is
+  // uniform.
   const char* kp = (const char*)((const uint16_t*)a.k + b * a.ks0 + kvh * a.ks1);
   const int64_t rowstride = a.ks2 * 2;  // bytes
   const uint32_t rs32 = (uint32_t)rowstride;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  uint32_t loff[2];
+#pragma unroll
+  for (int par = 0; par < 2; ++par) {
+    const int rr = lane >> 3;
+    loff[par] = (uint32_t)rr * rs32 + ((((lane & 7) ^ mla_f(8 * par + rr))) << 4);
+  }
+  // Copies go through a buffer resource per (tile, block row): its range ends
+  // at the last key of the cache, and the hardware returns zeros for rows
+  // past it (their scores are masked below and their values meet p = 0).
   auto tile_to_lds = [&](char* tile, int j) __attribute__((always_inline)) {
     const int c0 = j * BC;
-    const char* tp = kp + (int64_t)c0 * rowstride;
-    int ln0 = lane;
-    asm volatile("" : "+v"(ln0));
-    if (c0 + BC <= Nk) {
 #pragma unroll
-      for (int i = 0; i < DMA_PER_WAVE; ++i) {
-        const int p = 64 * (DMA_PER_WAVE * w + i) + ln0;
-        const int r = p / (DQK / 8), pc = p % (DQK / 8);
-        const uint32_t off = (uint32_t)r * rs32 + (uint32_t)((pc ^ mla_f(r)) << 4);
-        lds_dma16(tp + off, tile + 1024 * (DMA_PER_WAVE * w + i));
-      }
-    } else {
-      // rows past the end of the cache re-read its last row (masked below);
-      // the row index is recomputed here so that nothing of this path is kept
-      // live across the tile loop
-      int ln = lane;
-      asm volatile("" : "+v"(ln));
-      const int last = Nk - 1 - c0;
-#pragma unroll
-      for (int i = 0; i < DMA_PER_WAVE; ++i) {
-        const int r = (64 * (DMA_PER_WAVE * w + i) + ln) / (DQK / 8);
-        const int rr = min(r, last);
-        lds_dma16(tp + ((uint32_t)rr * rs32 + (uint32_t)((((64 * (DMA_PER_WAVE * w + i) + ln) % (DQK / 8)) ^ mla_f(r)) << 4)), tile + 1024 * (DMA_PER_WAVE * w + i));
-      }
+    for (int r2 = 0; r2 < 2; ++r2) {
+      // all uniform; readfirstlane tells the compiler so (no waterfall loop)
+      const int row0t = __builtin_amdgcn_readfirstlane(c0 + 16 * wu + 8 * r2);  // first key
+      const int nrec = __builtin_amdgcn_readfirstlane(min(max(Nk - row0t, 0), 8) * (int)rs32);
+      const uint64_t base = (uint64_t)(kp + (int64_t)row0t * rowstride);
+      const uint64_t ubase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32)) << 32) |
+                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+      const __amdgpu_buffer_rsrc_t rs =
+          __builtin_amdgcn_make_buffer_rsrc((void*)ubase, (short)0, nrec, kBufferFlags);
+      copy_block_row(rs, tile + 1024 * (DMA_PER_WAVE * wu + (DQK / 64) * r2), loff[r2],
+                     std::make_integer_sequence<int, DQK / 64>{});
     }
   };
 
-  f32x4_t o[8][4];  // O^T[dv = 128w + 16db + 4g + i][head 16hb + n]
+  f32x16_t o[4][2];  // O^T[dv = 128w + 32db + 8(i/4) + 4h + i%4][head 32hb + l32]
 #pragma unroll
-  for (int db = 0; db < 8; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb) o[db][hb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-  float m[2] = {m_init[0], m_init[1]};  // running max of the score heads (raw units)
-  float lp[2] = {0.f, 0.f};             // partial row sums over this lane's keys
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o[db][hb][i] = 0.f;
+  float m = m_init;      // exact running max of head hl (raw units): the decisions
+  float m_acc = m_init;  // reference max of the accumulators (lags m by < 2^8 in exp2 units)
+  float lp = 0.f;        // partial row sum over this lane's keys (fp32 p): the lse
+  float lq = 0.f;        // the same over the bf16-rounded p that P.V uses: the output
+                         // is normalised by it, so rounding a dominant p cancels
 
   // one key tile; the LDS buffer parity is a compile-time constant so that the
   // compiler can tell the copy into one buffer from the reads of the other
@@ -329,125 +376,115 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
     __syncthreads();  // (C) tile idx is in LDS; every wave is done with tile idx-1
     if (idx + 1 < nl) tile_to_lds(P ? Kt0 : Kt1, tile_of(idx + 1));
 
-    // scores: S^T[key 32kh + 16kb + 4g + i][head hl[hb]]
-    f32x4_t sc[2][2];
+    // scores S^T[key 32kh + 8(i/4) + 4h + i%4][head hl]: 36 steps on two
+    // accumulator chains, each step's K operand read four steps ahead
+    f32x16_t s0, s1;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < 16; ++i) s0[i] = s1[i] = 0.f;
+    u32x4_t kbuf[4];
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) sc[kb][hb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
-    // the two key-block operands of step kk are read one step ahead; the
-    // scheduling fence stops the compiler from hoisting every read of the
-    // tile (that would take 144 registers)
-    u32x4_t k0 = *(const u32x4_t*)(kt + ko_even);
-    u32x4_t k1 = *(const u32x4_t*)(kt + ko_even + 16 * ROWB);
+    for (int x = 0; x < 4; ++x) kbuf[x] = *(const u32x4_t*)(kt + ko[x]);
 #pragma unroll
-    for (int kk = 0; kk < KS; ++kk) {
-      u32x4_t n0 = k0, n1 = k1;
-      if (kk + 1 < KS) {
-        const int ko = (((kk + 1) & 1) ? ko_odd : ko_even) + 128 * ((kk + 1) >> 1);
-        n0 = *(const u32x4_t*)(kt + ko);
-        n1 = *(const u32x4_t*)(kt + ko + 16 * ROWB);
-      }
-      sc[0][0] = mfma16x16x32(as_bf16x8(k0), qb[0][kk], sc[0][0]);
-      sc[0][1] = mfma16x16x32(as_bf16x8(k0), qb[1][kk], sc[0][1]);
-      sc[1][0] = mfma16x16x32(as_bf16x8(k1), qb[0][kk], sc[1][0]);
-      sc[1][1] = mfma16x16x32(as_bf16x8(k1), qb[1][kk], sc[1][1]);
-      k0 = n0;
-      k1 = n1;
+    for (int kk = 0; kk < KS2; ++kk) {
+      const u32x4_t cur = kbuf[kk & 3];
+      if (kk + 4 < KS2) kbuf[kk & 3] = *(const u32x4_t*)(kt + ko[kk & 3] + 1024 * ((kk + 4) >> 2));
+      if (kk & 1) s1 = mfma32x32x16(as_bf16x8(cur), qb[kk], s1);
+      else s0 = mfma32x32x16(as_bf16x8(cur), qb[kk], s0);
       __builtin_amdgcn_sched_barrier(0);
     }
+    f32x16_t sc = s0 + s1;
     const int c0 = j * BC;
     if (c0 + BC > Nk) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (c0 + 32 * kh + 16 * kb + 4 * g + i >= Nk) sc[kb][0][i] = sc[kb][1][i] = kNegInf;
+      for (int i = 0; i < 16; ++i)
+        if (c0 + 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3) >= Nk) sc[i] = kNegInf;
     }
+    float tm = sc[0];
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      float tm = kNegInf;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        tm = fmaxf(tm, fmaxf(fmaxf(sc[kb][hb][0], sc[kb][hb][1]), fmaxf(sc[kb][hb][2], sc[kb][hb][3])));
-      tm = fmaxf(tm, shfl_xor_f(tm, 16));
-      tm = fmaxf(tm, shfl_xor_f(tm, 32));
-      if (g == 0) tmw[P][kh][hl[hb]] = tm;
-    }
+    for (int i = 1; i < 16; ++i) tm = fmaxf(tm, sc[i]);
+    tm = max_with_lane_xor32(tm);
+    if (h == 0) tmw[P][kh][hl] = tm;
     lds_barrier();  // (A) tile maxima of both key halves visible
 
-    bool anykeep = false, anyscale = false;
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      const float TM = fmaxf(tmw[P][0][hl[hb]], tmw[P][1][hl[hb]]);
-      if constexpr (MODE == 0) {
-        if (kh == 0 && g == 0 && hv[hb]) tmaxp[(row0 + hl[hb]) * nkt + j] = TM;
-      }
-      const bool keep = hv[hb] && (j == 0 || !(gap_of(TM, m[hb]) < thr));
-      float alpha = 1.f;
-      float p[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-      if (keep) {
-        const float m_new = fmaxf(m[hb], TM);
-        const float mc = m_new * c2;
-        if (m_new != m[hb]) {
-          alpha = fast_exp2(m[hb] * c2 - mc);
-          lp[hb] *= alpha;
-        }
-        m[hb] = m_new;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[kb][i] = fast_exp2(fmaf(sc[kb][hb][i], c2, -mc));
-            lp[hb] += p[kb][i];
-          }
-      }
-      anykeep |= keep;
-      anyscale |= alpha != 1.f;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-        *(u32x2_t*)&Ps[hl[hb] * PP + 32 * kh + 16 * kb + 4 * g] =
-            (u32x2_t){pack_bf16x2(p[kb][0], p[kb][1]), pack_bf16x2(p[kb][2], p[kb][3])};
-      if (kh == 0 && g == 0) alph[hl[hb]] = alpha;
+    const float TM = fmaxf(tmw[P][0][hl], tmw[P][1][hl]);
+    if constexpr (MODE == 0) {
+      if (kh == 0 && h == 0 && hv) tmaxp[(int64_t)j * G + hl] = TM;
     }
-    const uint64_t kb_ = __ballot(anykeep), sb_ = __ballot(anyscale);
+    const bool keep = hv && (j == 0 || !(gap_of(TM, m) < thr));
+    float alpha = 1.f;
+    uint32_t pw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+    if (keep) {
+      // lazy rescale: the accumulators keep their reference max until the
+      // running max exceeds it by 2^8 in exp2 units (p then stays <= 256,
+      // exact in fp32 and in range for bf16); decisions use the exact max
+      m = fmaxf(m, TM);
+      if (m_acc == kNegInf) {
+        m_acc = m;  // nothing accumulated yet
+      } else if ((m - m_acc) * c2 > kLazyRescaleLog2) {
+        alpha = fast_exp2((m_acc - m) * c2);
+        lp *= alpha;
+        lq *= alpha;
+        m_acc = m;
+      }
+      const float mc = m_acc * c2;
+#pragma unroll
+      for (int x = 0; x < 8; ++x) {
+        const float p0 = fast_exp2(fmaf(sc[2 * x], c2, -mc));
+        const float p1 = fast_exp2(fmaf(sc[2 * x + 1], c2, -mc));
+        lp += p0 + p1;
+        pw[x] = pack_bf16x2(p0, p1);
+        lq += bf16_lo(pw[x]) + bf16_hi(pw[x]);
+      }
+    }
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4)
+      *(u32x2_t*)&Ps[hl * PP + 32 * kh + 8 * q4 + 4 * h] = (u32x2_t){pw[2 * q4], pw[2 * q4 + 1]};
+    if (kh == 0 && h == 0) alph[hl] = alpha;
+    const uint64_t kb_ = __ballot(keep), sb_ = __ballot(alpha != 1.f);
     if (lane == 0) kflag[w] = (kb_ ? 1 : 0) | (sb_ ? 2 : 0);
     lds_barrier();  // (B) P^T, rescale factors and flags visible
     const int fl = kflag[0] | kflag[1] | kflag[2] | kflag[3];
     if (fl & 2) {
 #pragma unroll
-      for (int hb = 0; hb < 4; ++hb) {
-        const float al = alph[16 * hb + n];
+      for (int hb = 0; hb < 2; ++hb) {
+        const float al = alph[32 * hb + l32];
 #pragma unroll
-        for (int db = 0; db < 8; ++db) o[db][hb] *= al;
+        for (int db = 0; db < 4; ++db) o[db][hb] *= al;
       }
     }
     if (fl & 1) {
+      // O^T += V^T P^T over 4 steps of 16 keys; each step's operands are read
+      // one step ahead
+      auto rd = [&](int ks, u32x4_t (&va)[4], u32x4_t (&pb)[2]) __attribute__((always_inline)) {
+        const char* vk = kt + 16 * ks * ROWB;  // two block rows
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        bf16x8_t pb[4];
-#pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-          pb[hb] = as_bf16x8(*(const u32x4_t*)&Ps[(16 * hb + n) * PP + 32 * cc + 8 * g]);
-        const char* vc = kt + cc * 32 * ROWB;
-        // value operands read one output block ahead, fenced as above
-        u32x2_t y0 = ds_read_tr(vc + vo[0][0]);
-        u32x2_t y1 = ds_read_tr(vc + vo[0][1]);
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-          u32x2_t z0 = y0, z1 = y1;
-          if (db + 1 < 8) {
-            const int off = ((db + 1) >> 2) * 128;
-            z0 = ds_read_tr(vc + off + vo[(db + 1) & 3][0]);
-            z1 = ds_read_tr(vc + off + vo[(db + 1) & 3][1]);
-          }
-          const bf16x8_t va = as_bf16x8((u32x4_t){y0[0], y0[1], y1[0], y1[1]});
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb) o[db][hb] = mfma16x16x32(va, pb[hb], o[db][hb]);
-          y0 = z0;
-          y1 = z1;
-          __builtin_amdgcn_sched_barrier(0);
+        for (int db = 0; db < 4; ++db) {
+          const u32x2_t y0 = ds_read_tr(vk + 1024 * (db >> 1) + vo[db & 1][0]);
+          const u32x2_t y1 = ds_read_tr(vk + 1024 * (db >> 1) + vo[db & 1][1]);
+          va[db] = (u32x4_t){y0[0], y0[1], y1[0], y1[1]};
         }
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          pb[hb] = *(const u32x4_t*)&Ps[(32 * hb + l32) * PP + 16 * ks + 8 * h];
+      };
+      u32x4_t va[4], pb[2];
+      rd(0, va, pb);
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        u32x4_t van[4], pbn[2];
+        if (ks + 1 < 4) rd(ks + 1, van, pbn);
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+            o[db][hb] = mfma32x32x16(as_bf16x8(va[db]), as_bf16x8(pb[hb]), o[db][hb]);
+        if (ks + 1 < 4) {
+#pragma unroll
+          for (int db = 0; db < 4; ++db) va[db] = van[db];
+          pb[0] = pbn[0];
+          pb[1] = pbn[1];
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     ++idx;
@@ -462,29 +499,31 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
   }
 
   // ---- partial of this split: (m, l) per head and the unnormalised O
-#pragma unroll
-  for (int hb = 0; hb < 2; ++hb) {
-    float l = lp[hb];
-    l += shfl_xor_f(l, 16);
-    l += shfl_xor_f(l, 32);
-    if (g == 0) lred[kh][hl[hb]] = l;
+  const float lsum = sum_with_lane_xor32(lp);
+  const float qsum = sum_with_lane_xor32(lq);
+  if (h == 0) {
+    lred[0][kh][hl] = lsum;
+    lred[1][kh][hl] = qsum;
   }
   __syncthreads();
-  if (kh == 0 && g == 0) {
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-      if (hv[hb]) {
-        float* ml = ws.part_ml + ((row0 + hl[hb]) * nsplit + s) * 2;
-        ml[0] = m[hb];
-        ml[1] = lred[0][hl[hb]] + lred[1][hl[hb]];
-      }
+  if (kh == 0 && h == 0 && hv) {
+    float* ml = ws.part_ml + ((row0 + hl) * nsplit + s) * 4;
+    ml[0] = m_acc;
+    ml[1] = lred[0][0][hl] + lred[0][1][hl];
+    ml[2] = lred[1][0][hl] + lred[1][1][hl];
+    if constexpr (MODE == 0) ws.smax[(row0 + hl) * nsplit + s] = m;
   }
 #pragma unroll
-  for (int hb = 0; hb < 4; ++hb) {
-    if (h0 + 16 * hb + n >= G) continue;
-    float* po = ws.part_o + ((row0 + 16 * hb + n) * nsplit + s) * DV + 128 * w + 4 * g;
+  for (int hb = 0; hb < 2; ++hb) {
+    if (h0 + 32 * hb + l32 >= G) continue;
+    float* po = ws.part_o + ((row0 + 32 * hb + l32) * nsplit + s) * DV + 128 * w + 4 * h;
 #pragma unroll
-    for (int db = 0; db < 8; ++db) *(f32x4_t*)(po + 16 * db) = o[db][hb];
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *(f32x4_t*)(po + 32 * db + 8 * q4) =
+            (f32x4_t){o[db][hb][4 * q4], o[db][hb][4 * q4 + 1], o[db][hb][4 * q4 + 2],
+                      o[db][hb][4 * q4 + 3]};
   }
 }
 
@@ -498,22 +537,23 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(DecodeArgs a, Mla
   const int kvh = hq / a.G;
   const int nsplit = ws.nsplit;
   const float c2 = a.scale_log2;
-  const float* ml = ws.part_ml + row * nsplit * 2;
+  const float* ml = ws.part_ml + row * nsplit * 4;
   float ms = kNegInf;
   for (int s = 0; s < nsplit; ++s)
-    if (ml[2 * s + 1] > 0.f) ms = fmaxf(ms, ml[2 * s]);
-  float L = 0.f;
+    if (ml[4 * s + 1] > 0.f) ms = fmaxf(ms, ml[4 * s]);
+  float L = 0.f, Lq = 0.f;
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
   for (int s = 0; s < nsplit; ++s) {
-    const float l = ml[2 * s + 1];
+    const float l = ml[4 * s + 1];
     if (!(l > 0.f)) continue;
-    const float wgt = fast_exp2((ml[2 * s] - ms) * c2);
+    const float wgt = fast_exp2((ml[4 * s] - ms) * c2);
     L += l * wgt;
+    Lq += ml[4 * s + 2] * wgt;
     const float* po = ws.part_o + (row * nsplit + s) * DV + 8 * lane;
     acc0 += *(const f32x4_t*)po * wgt;
     acc1 += *(const f32x4_t*)(po + 4) * wgt;
   }
-  const float inv = 1.f / L;
+  const float inv = 1.f / Lq;
   const int64_t ob = b * a.os0 + (int64_t)hq * a.os1 + 8 * lane;
   store_out4(a.out, ob, a.out_f32, acc0[0] * inv, acc0[1] * inv, acc0[2] * inv, acc0[3] * inv);
   store_out4(a.out, ob + 4, a.out_f32, acc1[0] * inv, acc1[1] * inv, acc1[2] * inv, acc1[3] * inv);
@@ -545,7 +585,7 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(DecodeArgs a, Mla
 namespace {
 struct MlaPlan {
   int ngroups, nsplit, T;
-  size_t off_tmax, off_o, off_ml, off_kept, off_any, bytes;
+  size_t off_tmax, off_smax, off_o, off_ml, off_kept, off_any, bytes;
 };
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -564,10 +604,12 @@ MlaPlan mla_plan(int B, int Hq, int Hkv, int G, int nkt) {
   size_t off = 0;
   p.off_tmax = off;
   off = align256(off + rows * nkt * sizeof(float));
+  p.off_smax = off;
+  off = align256(off + rows * p.nsplit * sizeof(float));
   p.off_o = off;
   off = align256(off + rows * p.nsplit * DV * sizeof(float));
   p.off_ml = off;
-  off = align256(off + rows * p.nsplit * 2 * sizeof(float));
+  off = align256(off + rows * p.nsplit * 4 * sizeof(float));
   p.off_kept = off;
   off = align256(off + rows * p.nsplit * sizeof(int));
   p.off_any = off;
@@ -586,6 +628,7 @@ hipError_t launch_decode_mla(const DecodeArgs& a, void* workspace, hipStream_t s
   char* base = static_cast<char*>(workspace);
   MlaWork ws;
   ws.tmax = reinterpret_cast<float*>(base + p.off_tmax);
+  ws.smax = reinterpret_cast<float*>(base + p.off_smax);
   ws.part_o = reinterpret_cast<float*>(base + p.off_o);
   ws.part_ml = reinterpret_cast<float*>(base + p.off_ml);
   ws.part_kept = reinterpret_cast<int*>(base + p.off_kept);

@@ -134,7 +134,7 @@ def test_prefill_validation(case, expect):
 @pytest.mark.parametrize("case,expect", [
     ("len_q", 2), ("latent_dv", 2), ("gqa_too_many_heads", 6), ("bad_bc", 6),
     ("null_k", 1), ("lam", 4), ("f32", 6), ("mla_no_workspace", 9),
-    ("mla_small_workspace", 9), ("mla_misaligned_workspace", 9),
+    ("mla_small_workspace", 9), ("mla_misaligned_workspace", 9), ("mla_overlapping_rows", 2),
 ])
 def test_decode_validation(case, expect):
     sh = _shape(Hq=8, Hkv=2, Nq=1, Nk=1000)
@@ -156,6 +156,9 @@ def test_decode_validation(case, expect):
             kw["ws"], kw["ws_bytes"] = P, need - 1
         elif case == "mla_misaligned_workspace":
             kw["ws"], kw["ws_bytes"] = P + 16, need
+        elif case == "mla_overlapping_rows":
+            kw["ws"], kw["ws_bytes"] = P, need
+            sh.k_stride[2] = 512
     elif case == "null_k":
         kw["k"] = None
     elif case == "lam":

@@ -141,7 +141,8 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
   __shared__ float alph[HG];
   __shared__ float lred[2][2][HG];  // [sum kind][key half][head]
   __shared__ int kflag[NW];
-  __shared__ uint16_t list[LIST_MAX];  // kept tiles of the split, relative to its first
+  __shared__ uint16_t list[LIST_MAX];  // pass 1: tiles to correct, relative to the split start
+  __shared__ uint64_t lmask[LIST_MAX]; // pass 1: heads whose contribution of that tile is removed
   __shared__ float mstart[HG];         // exact running max entering the split
   __shared__ int cntw[NW][HG];
   __shared__ int misw[NW];
@@ -184,12 +185,18 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
   // ---- exact decisions (pass 1): true running max entering the split, mask,
   // counts, and whether pass 0 took the same decisions
   float m_init = kNegInf;
-  int nl = j1 - j0;
+  // pass 0 of a split after the first scores tile 0 (which holds the attention
+  // sinks) before its own tiles: its maxima start the split's running max, a
+  // lower bound of the exact one that usually equals it, so the speculative
+  // decisions usually are the exact ones
+  const int pre = (MODE == 0 && s > 0) ? 1 : 0;
+  int nl = j1 - j0 + pre;
   if constexpr (MODE == 1) {
     const int tn = j1 - j0;
     float* tms = reinterpret_cast<float*>(Kt1);   // [tn][HG] tile maxima of the split
     uint8_t* mk = reinterpret_cast<uint8_t*>(Kt0);  // [HG][LIST_MAX] exact decisions
     uint8_t* tflag = mk + HG * LIST_MAX;             // [tn] some head keeps the tile
+    uint64_t* cm = reinterpret_cast<uint64_t*>(Kt1 + 4 * HG * LIST_MAX);  // [tn] heads to correct
     const int hp = lane;  // one head per lane
     const bool hvp = h0 + hp < G;
     // the split's tile maxima into LDS, 16 independent loads per wave at a time
@@ -221,7 +228,8 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
     // follow from the tiles before it (a dropped tile's max is below the
     // running max, so the plain max is the running max over kept tiles)
     const int q0 = (w * tn) / NW, q1 = ((w + 1) * tn) / NW;
-    float ml = kNegInf;  // as pass 0 had it: from the split's first tile
+    // as pass 0 had it: from tile 0 (splits after the first) and the split's tiles
+    float ml = (s > 0 && hvp) ? tmaxp[hp] : kNegInf;
     for (int jj = 0; jj < q0; ++jj) ml = fmaxf(ml, tms[jj * HG + hp]);
     float mt = fmaxf(mstart[hp], ml);  // exact: from tile 0
     int cnt = 0;
@@ -235,12 +243,17 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
       mt = fmaxf(mt, tm);
       ml = fmaxf(ml, tm);
       cnt += kt ? 1 : 0;
-      mis |= kt != kl;
       mk[hp * LIST_MAX + jj] = kt ? 1 : 0;
+      // the exact rule never keeps a tile the speculative one dropped (its
+      // running max is at least as large); a tile kept only speculatively has
+      // its contribution removed below
+      const uint64_t corr = __ballot(kl && !kt);
+      mis |= corr != 0;
       const bool any = __ballot(kt) != 0;
       if (lane == 0) {
         tflag[jj] = any ? 1 : 0;
         anyrow[jj] = any ? 1 : 0;
+        cm[jj] = corr;
       }
     }
     cntw[w][hp] = cnt;
@@ -258,24 +271,28 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
       ws.part_kept[(row0 + hp) * nsplit + s] = cntw[0][hp] + cntw[1][hp] + cntw[2][hp] + cntw[3][hp];
     const bool redo = (misw[0] | misw[1] | misw[2] | misw[3]) != 0;
     if (!redo) return;  // the pass-0 partial is already exact
-    m_init = mstart[hl];
-    // list of the tiles some head keeps, in order
+    // list of the tiles to correct, in order, with their head masks
     if (w == 0) {
       int base = 0;
       for (int c0 = 0; c0 < tn; c0 += 64) {
-        const bool f = c0 + lane < tn && tflag[c0 + lane] != 0;
+        const uint64_t mk64 = c0 + lane < tn ? cm[c0 + lane] : 0ull;
+        const bool f = mk64 != 0ull;
         const uint64_t bits = __ballot(f);
-        if (f) list[base + __popcll(bits & ((1ull << lane) - 1ull))] = (uint16_t)(c0 + lane);
+        if (f) {
+          const int at = base + __popcll(bits & ((1ull << lane) - 1ull));
+          list[at] = (uint16_t)(c0 + lane);
+          lmask[at] = mk64;
+        }
         base += __popcll(bits);
       }
       if (lane == 0) nlist = base;
     }
-    __syncthreads();  // list ready; mk and tms (in the tile buffers) no longer read
+    __syncthreads();  // list ready; mk, tms and cm (in the tile buffers) no longer read
     nl = nlist;
   }
   auto tile_of = [&](int idx) __attribute__((always_inline)) -> int {
     if constexpr (MODE == 1) return j0 + __builtin_amdgcn_readfirstlane((int)list[idx]);
-    else return j0 + idx;
+    else return idx < pre ? 0 : j0 + idx - pre;
   };
 
   // ---- queries: q^T as the B operand of v_mfma_f32_32x32x16_bf16, lane
@@ -353,14 +370,33 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
   };
 
   f32x16_t o[4][2];  // O^T[dv = 128w + 32db + 8(i/4) + 4h + i%4][head 32hb + l32]
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) o[db][hb][i] = 0.f;
   float m = m_init;      // exact running max of head hl (raw units): the decisions
   float m_acc = m_init;  // reference max of the accumulators (lags m by < 2^8 in exp2 units)
+  if constexpr (MODE == 0) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o[db][hb][i] = 0.f;
+  } else {
+    // the correction starts from the pass-0 partial and keeps its reference max
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const bool v = h0 + 32 * hb + l32 < G;
+      const float* po = ws.part_o + ((row0 + (v ? 32 * hb + l32 : 0)) * nsplit + s) * DV + 128 * w + 4 * h;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          f32x4_t x = *(const f32x4_t*)(po + 32 * db + 8 * q4);
+          if (!v) x = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[db][hb][4 * q4 + e] = x[e];
+        }
+    }
+    m_acc = hv ? ws.part_ml[((row0 + hl) * nsplit + s) * 4] : 0.f;
+  }
   float lp = 0.f;        // partial row sum over this lane's keys (fp32 p): the lse
   float lq = 0.f;        // the same over the bf16-rounded p that P.V uses: the output
                          // is normalised by it, so rounding a dominant p cancels
@@ -399,41 +435,60 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
       for (int i = 0; i < 16; ++i)
         if (c0 + 32 * kh + 8 * (i >> 2) + 4 * h + (i & 3) >= Nk) sc[i] = kNegInf;
     }
-    float tm = sc[0];
-#pragma unroll
-    for (int i = 1; i < 16; ++i) tm = fmaxf(tm, sc[i]);
-    tm = max_with_lane_xor32(tm);
-    if (h == 0) tmw[P][kh][hl] = tm;
-    lds_barrier();  // (A) tile maxima of both key halves visible
-
-    const float TM = fmaxf(tmw[P][0][hl], tmw[P][1][hl]);
-    if constexpr (MODE == 0) {
-      if (kh == 0 && h == 0 && hv) tmaxp[(int64_t)j * G + hl] = TM;
-    }
-    const bool keep = hv && (j == 0 || !(gap_of(TM, m) < thr));
+    bool keep = false;
     float alpha = 1.f;
     uint32_t pw[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
-    if (keep) {
-      // lazy rescale: the accumulators keep their reference max until the
-      // running max exceeds it by 2^8 in exp2 units (p then stays <= 256,
-      // exact in fp32 and in range for bf16); decisions use the exact max
-      m = fmaxf(m, TM);
-      if (m_acc == kNegInf) {
-        m_acc = m;  // nothing accumulated yet
-      } else if ((m - m_acc) * c2 > kLazyRescaleLog2) {
-        alpha = fast_exp2((m_acc - m) * c2);
-        lp *= alpha;
-        lq *= alpha;
-        m_acc = m;
-      }
-      const float mc = m_acc * c2;
+    if constexpr (MODE == 0) {
+      float tm = sc[0];
 #pragma unroll
-      for (int x = 0; x < 8; ++x) {
-        const float p0 = fast_exp2(fmaf(sc[2 * x], c2, -mc));
-        const float p1 = fast_exp2(fmaf(sc[2 * x + 1], c2, -mc));
-        lp += p0 + p1;
-        pw[x] = pack_bf16x2(p0, p1);
-        lq += bf16_lo(pw[x]) + bf16_hi(pw[x]);
+      for (int i = 1; i < 16; ++i) tm = fmaxf(tm, sc[i]);
+      tm = max_with_lane_xor32(tm);
+      if (h == 0) tmw[P][kh][hl] = tm;
+      lds_barrier();  // (A) tile maxima of both key halves visible
+
+      const float TM = fmaxf(tmw[P][0][hl], tmw[P][1][hl]);
+      const bool sink_only = idx < pre;  // tile 0 scored by a later split: max only
+      if (sink_only && hv) m = fmaxf(m, TM);
+      if (!sink_only && kh == 0 && h == 0 && hv) tmaxp[(int64_t)j * G + hl] = TM;
+      keep = !sink_only && hv && (j == 0 || !(gap_of(TM, m) < thr));
+      if (keep) {
+        // lazy rescale: the accumulators keep their reference max until the
+        // running max exceeds it by 2^8 in exp2 units (p then stays <= 256,
+        // exact in fp32 and in range for bf16); decisions use the exact max
+        m = fmaxf(m, TM);
+        if (m_acc == kNegInf) {
+          m_acc = m;  // nothing accumulated yet
+        } else if ((m - m_acc) * c2 > kLazyRescaleLog2) {
+          alpha = fast_exp2((m_acc - m) * c2);
+          lp *= alpha;
+          lq *= alpha;
+          m_acc = m;
+        }
+        const float mc = m_acc * c2;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const float p0 = fast_exp2(fmaf(sc[2 * x], c2, -mc));
+          const float p1 = fast_exp2(fmaf(sc[2 * x + 1], c2, -mc));
+          lp += p0 + p1;
+          pw[x] = pack_bf16x2(p0, p1);
+          lq += bf16_lo(pw[x]) + bf16_hi(pw[x]);
+        }
+      }
+    } else {
+      // correction: this tile was kept by pass 0 for the heads in the mask
+      // and is dropped by the exact rule; its contribution at the partial's
+      // reference max is subtracted (same p, negated)
+      keep = hv && ((lmask[idx] >> hl) & 1ull) != 0ull;
+      if (keep) {
+        const float mc = m_acc * c2;
+#pragma unroll
+        for (int x = 0; x < 8; ++x) {
+          const float p0 = -fast_exp2(fmaf(sc[2 * x], c2, -mc));
+          const float p1 = -fast_exp2(fmaf(sc[2 * x + 1], c2, -mc));
+          lp += p0 + p1;
+          pw[x] = pack_bf16x2(p0, p1);
+          lq += bf16_lo(pw[x]) + bf16_hi(pw[x]);
+        }
       }
     }
 #pragma unroll
@@ -508,10 +563,17 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
   __syncthreads();
   if (kh == 0 && h == 0 && hv) {
     float* ml = ws.part_ml + ((row0 + hl) * nsplit + s) * 4;
-    ml[0] = m_acc;
-    ml[1] = lred[0][0][hl] + lred[0][1][hl];
-    ml[2] = lred[1][0][hl] + lred[1][1][hl];
-    if constexpr (MODE == 0) ws.smax[(row0 + hl) * nsplit + s] = m;
+    const float dl = lred[0][0][hl] + lred[0][1][hl];
+    const float dq = lred[1][0][hl] + lred[1][1][hl];
+    if constexpr (MODE == 0) {
+      ml[0] = m_acc;
+      ml[1] = dl;
+      ml[2] = dq;
+      ws.smax[(row0 + hl) * nsplit + s] = m;
+    } else {
+      ml[1] += dl;  // the removed contributions (negative)
+      ml[2] += dq;
+    }
   }
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {

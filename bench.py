@@ -125,7 +125,7 @@ def read_traffic(kind: str, sha: str):
         d = json.load(f)
     if d.get("kernel_source_sha") != sha:
         return None, "kernel changed since the counters were taken"
-    return d.get("hbm_bytes_per_launch"), path
+    return d.get("hbm_bytes_per_launch"), os.path.relpath(path, os.path.dirname(PROFILE_DIR))
 
 
 # --------------------------------------------------------------------------- legs

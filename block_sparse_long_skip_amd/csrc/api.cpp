@@ -151,6 +151,8 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
                 "64/64 64x64, bf16 128/128 128x64)",
                 (int)dtype, s.d_qk, s.d_v, br, bc);
   // the bf16 kernel addresses a 64-row tile with 32-bit per-lane byte offsets
+  if (b16 && (s.k_stride[2] < s.d_qk || s.v_stride[2] < s.d_v))
+    return fail(BLASST_E_SHAPE, "key/value rows overlap (position stride below the row length)");
   if (b16 && (s.k_stride[2] > (1 << 24) || s.v_stride[2] > (1 << 24)))
     return fail(BLASST_E_UNSUPPORTED, "bf16 prefill needs key/value position strides <= 2^24 elements");
   const int64_t nqt = ((int64_t)s.len_q + br - 1) / br;

@@ -40,10 +40,10 @@
 // LDS: K and V tiles double-buffered, 64 rows x 256 B each, unpadded, with the
 // 16-byte chunk index XOR-swizzled by the row so that both the K operand reads
 // (16 rows, one chunk) and the transposing V reads (4 rows, 2 chunks) hit
-// distinct banks. Tiles travel global -> LDS with global_load_lds_dwordx4 (no
-// register staging). Every per-lane address is computed once before the loop:
-// LDS reads are a per-lane base plus immediate offsets, tile loads a uniform
-// tile pointer plus a per-lane 32-bit offset.
+// distinct banks. Tiles travel global -> LDS with buffer_load_dwordx4 ... lds
+// (no register staging): a buffer resource per tile (uniform base and range),
+// a per-lane 32-bit offset fixed for the whole loop, and no vector ALU work
+// per copy. LDS reads are a per-lane base plus immediate offsets.
 #include <type_traits>
 
 #include "common.hpp"
@@ -57,6 +57,7 @@ constexpr int BC = 64;
 constexpr int NT = 256;
 constexpr int TILE_BYTES = BC * D * 2;  // 16 KB
 constexpr float kLazyRescaleLog2 = 8.f;  // rescale once the max grows by 2^8
+constexpr int kBufferFlags = 0x00020000;   // buffer resource word 3: 32-bit data format, raw access
 
 // XOR applied to the 16-byte chunk index of tile row `row`
 __device__ __forceinline__ int swz_f(int row) { return ((row & 3) << 2) | ((row >> 2) & 3); }
@@ -126,23 +127,25 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     koff[r] = (uint32_t)(((int64_t)trow * a.ks2 + ch * 8) * 2);
     voff[r] = (uint32_t)(((int64_t)trow * a.vs2 + ch * 8) * 2);
   }
-  // One tile into LDS. Rows past the end of the sequence are clamped to its
-  // last row: their scores are masked to -inf, so they never contribute.
+  // One tile into LDS through a buffer resource whose range ends at the last
+  // key of the sequence: the hardware returns zeros for rows past it (their
+  // scores are masked to -inf, and their values meet p = 0). The per-lane
+  // offsets above do not depend on the tile; base, range and LDS address are
+  // uniform.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   auto tile_to_lds = [&](char* tile, const char* base, const uint32_t (&off)[4], int64_t stride,
                          int c0) {
-    if (c0 + BC <= a.Nk) {
-      const char* tp = base + (int64_t)c0 * stride * 2;
+    const uint64_t tb = (uint64_t)(base + (int64_t)c0 * stride * 2);
+    const uint64_t ub = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(tb >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tb);
+    const int rows = __builtin_amdgcn_readfirstlane(min(a.Nk - c0, BC));
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)ub, (short)0, (int)((uint32_t)rows * (uint32_t)(stride * 2)), kBufferFlags);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lds_dma16(tp + off[r], tile + (16 * w + 4 * r) * 256);
-    } else {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int trow = 16 * w + 4 * r + sub;
-        const int key = min(c0 + trow, a.Nk - 1);
-        const int ch = pch ^ swz_f(trow);
-        lds_dma16(base + ((int64_t)key * stride + ch * 8) * 2, tile + (16 * w + 4 * r) * 256);
-      }
-    }
+    for (int r = 0; r < 4; ++r)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rs, (__attribute__((address_space(3))) void*)(tile + (16 * wu + 4 * r) * 256), 16, off[r],
+          0, 0, 0);
   };
   // K operand reads: key row 32kb + l32, chunk 2kk + h (kb = 1 is +8192 bytes)
   int kro[D / 16];

@@ -83,7 +83,7 @@ def _err():
     ("causal_nq_gt_nk", 2), ("neg_len", 2), ("lam_neg", 4), ("lam_gt1", 4), ("lam_nan", 4),
     ("scale_inf", 7), ("misaligned_ptr", 5), ("misaligned_stride", 5), ("bad_d", 6),
     ("bad_tile", 6), ("f32_wrong_d", 6), ("zero_tile", 2), ("f32_in_bf16_out", 3),
-    ("bad_out_dtype", 3),
+    ("bad_out_dtype", 3), ("overlapping_kv_rows", 2),
 ])
 def test_prefill_validation(case, expect):
     sh = _shape()
@@ -127,6 +127,8 @@ def test_prefill_validation(case, expect):
         sh.d_qk = sh.d_v = 64
     elif case == "bad_out_dtype":
         kw["out_dtype"] = 9
+    elif case == "overlapping_kv_rows":
+        sh.k_stride[2] = 64
     assert _prefill(sh, **kw) == expect, _err()
     assert _err() != ""
 

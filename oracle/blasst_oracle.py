@@ -41,6 +41,10 @@ notes of the repository):
 * GQA: query head h reads key/value head h // (Hq / Hkv).
 * Decode is the same rule with one query row per (batch, head); tile 0 is
   the global first key tile and the running max is global along the keys.
+* Block-sparse mode: a (query, key) pair is visible when causality allows it
+  and its (query tile, key tile) block is in the caller's set; the skip rule
+  then runs over the set's tiles only, so "tile 0" is the first tile of the
+  set that the query tile visits. Rows that see nothing output zero, lse -inf.
 
 Arithmetic is float64 throughout; inputs are whatever float values the caller
 passes (bf16 workloads pass the exact bf16 values, widened).
@@ -127,7 +131,8 @@ def blasst_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, lam: float, bc: int
         m_before[j] = m
         tile_max[j] = mt
         # per-row gap with the infinity conventions, then the tile's max-gap
-        g_r = np.where(mt == -np.inf, -np.inf, np.where(m == -np.inf, np.inf, mt - m))
+        with np.errstate(invalid="ignore"):  # mt - m is discarded where either is -inf
+            g_r = np.where(mt == -np.inf, -np.inf, np.where(m == -np.inf, np.inf, mt - m))
         g = g_r.max() if rows else -np.inf
         gap[j] = g
         keep = (j == 0) or not (g < thr)
@@ -136,8 +141,10 @@ def blasst_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, lam: float, bc: int
             continue
         mask[j] = MASK_KEPT
         m_new = np.maximum(m, mt)
-        alpha = np.exp(m - m_new)       # 0 where m was -inf
-        p = np.exp(st - m_new[:, None])  # 0 where masked
+        # a row that has seen no key yet keeps empty sums (reference 0 instead of -inf)
+        m_ref = np.where(m_new == -np.inf, 0.0, m_new)
+        alpha = np.exp(m - m_ref)        # 0 where m was -inf
+        p = np.exp(st - m_ref[:, None])  # 0 where masked
         l = alpha * l + p.sum(axis=1)
         o = alpha[:, None] * o + p @ v[c0:c1]
         m = m_new
@@ -197,6 +204,60 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, lam: float, causal: boo
                 r0 = i * br
                 out[b, hq, r0:r0 + r.out.shape[0]] = r.out
                 lse[b, hq, r0:r0 + r.out.shape[0]] = r.lse
+                mask[b, hq, i] = r.mask
+                gap[b, hq, i] = r.gap
+            stats[b, hq, 0] = int((mask[b, hq] != MASK_NOT_VISITED).sum())
+            stats[b, hq, 1] = int((mask[b, hq] == MASK_KEPT).sum())
+    return OracleResult(out, lse, mask, gap, stats)
+
+
+def prefill_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_mask: np.ndarray,
+                   lam: float, causal: bool, br: int, bc: int,
+                   scale: Optional[float] = None) -> OracleResult:
+    """Prefill restricted to a caller-given set of (query tile, key tile) blocks.
+
+    Ordinary softmax attention computed only inside selected blocks is the
+    last stage of block-sparse prefill methods (the CRISP summary on rit.work,
+    section "Что сделали", last paragraph); block-sparse masks are one of the
+    mask kinds of the LongCA-bench post on denisavetisyan.com (section "Сад
+    Внимания: LongCA-bench и Стандартизация Оценки"). The skip rule runs inside
+    the set: the set's key tiles are visited in increasing order, the first one
+    a query tile visits is always kept (its rows have no running max yet, so
+    their gap is +inf), and the running max covers kept tiles of the set only.
+
+    block_mask: [B, Hq, nQt, nKt], broadcastable from the left; nonzero marks
+    a block the query tile may attend. A (query, key) pair is visible when the
+    causal rule allows it and its block is in the set. Blocks outside the set
+    are "not visited" (mask value 2). A row that sees no key at all gets a zero
+    output and lse = -inf.
+    """
+    B, Hq, nq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    dv = v.shape[3]
+    if Hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if causal and nq > nk:
+        raise ValueError("causal prefill needs Nq <= Nk")
+    if scale is None:
+        scale = default_scale(d)
+    nqt, nkt = -(-nq // br), -(-nk // bc)
+    sel = np.broadcast_to(np.asarray(block_mask) != 0, (B, Hq, nqt, nkt))
+    out = np.zeros((B, Hq, nq, dv))
+    lse = np.full((B, Hq, nq), -np.inf)
+    mask = np.full((B, Hq, nqt, nkt), MASK_NOT_VISITED, dtype=np.uint8)
+    gap = np.full((B, Hq, nqt, nkt), np.nan)
+    stats = np.zeros((B, Hq, 2), dtype=np.int64)
+    for b in range(B):
+        for hq in range(Hq):
+            kvh = hq // (Hq // hkv)
+            for i in range(nqt):
+                r0, r1 = i * br, min((i + 1) * br, nq)
+                in_set = np.repeat(sel[b, hq, i], bc)[:nk]
+                vis = visible(nq, nk, causal, r0, r1 - r0) & in_set[None, :]
+                r = blasst_rows(q[b, hq, r0:r1], k[b, kvh], v[b, kvh], lam, bc, vis, scale)
+                seen = vis.any(axis=1)
+                out[b, hq, r0:r1] = np.where(seen[:, None], r.out, 0.0)
+                lse[b, hq, r0:r1] = np.where(seen, r.lse, -np.inf)
                 mask[b, hq, i] = r.mask
                 gap[b, hq, i] = r.gap
             stats[b, hq, 0] = int((mask[b, hq] != MASK_NOT_VISITED).sum())
@@ -293,6 +354,7 @@ def masked_dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np
 
 __all__ = [
     "threshold", "default_scale", "visible", "blasst_rows", "prefill_tile", "prefill",
+    "prefill_masked",
     "decode_row", "decode", "naive_attention", "expand_tile_mask", "masked_dense_attention",
     "OracleResult", "TileRowResult", "MASK_SKIPPED", "MASK_KEPT", "MASK_NOT_VISITED",
 ]

@@ -216,11 +216,14 @@ def pin_closed_form_mask(orc):
             assert (r.mask == cf).all(), (lam, causal)
 
 
-def _brute(q, k, v, lam, causal, br, bc, scale):
+def _brute(q, k, v, lam, causal, br, bc, scale, sel=None):
     """Pure-Python loops straight from the definition, no incremental state.
 
     The running max before tile j is recomputed from scratch as the max score
     over the tiles kept so far; the output is a plain softmax over kept keys.
+    ``sel`` (optional [nQt][nKt] booleans) restricts attention to a block set:
+    a pair is visible only inside a selected block, and a row that sees no key
+    gets a zero output and lse -inf. Returns (mask, out, lse).
     """
     Nq, d = len(q), len(q[0])
     Nk = len(k)
@@ -231,10 +234,13 @@ def _brute(q, k, v, lam, causal, br, bc, scale):
         return scale * sum(q[r][x] * k[c][x] for x in range(d))
 
     def vis(r, c):
+        if sel is not None and not sel[r // br][c // bc]:
+            return False
         return (not causal) or c <= r + Nk - Nq
 
     mask = [[2] * nkt for _ in range(nqt)]
     out = [[0.0] * len(v[0]) for _ in range(Nq)]
+    lse = [-math.inf] * Nq
     for i in range(nqt):
         rows = range(i * br, min((i + 1) * br, Nq))
         kept = []
@@ -259,12 +265,15 @@ def _brute(q, k, v, lam, causal, br, bc, scale):
                 mask[i][j] = 0
         for r in rows:
             cs = [c for t in kept for c in range(t * bc, min((t + 1) * bc, Nk)) if vis(r, c)]
+            if not cs:
+                continue
             mx = max(score(r, c) for c in cs)
             w = [math.exp(score(r, c) - mx) for c in cs]
             den = sum(w)
+            lse[r] = mx + math.log(den)
             for x in range(len(v[0])):
                 out[r][x] = sum(wi * v[c][x] for wi, c in zip(w, cs)) / den
-    return mask, out
+    return mask, out, lse
 
 
 def pin_brute_force(orc):
@@ -280,9 +289,11 @@ def pin_brute_force(orc):
         q, k, v = _rand_case(rng, 1, 1, 1, Nq, Nk, d, 2, plant=float(rng.choice([0.0, 3.0])))
         sc = 1.0 / math.sqrt(d)
         r = orc.prefill(q, k, v, lam, causal, br, bc)
-        bm, bo = _brute(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), lam, causal, br, bc, sc)
+        bm, bo, bl = _brute(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), lam, causal, br,
+                            bc, sc)
         assert r.mask[0, 0].tolist() == bm, trial
         assert np.abs(r.out[0, 0] - np.array(bo)).max() < 1e-12, trial
+        assert np.abs(r.lse[0, 0] - np.array(bl)).max() < 1e-12, trial
 
 
 def pin_decode_sdpa(orc):
@@ -305,9 +316,136 @@ def pin_decode_sdpa(orc):
     assert np.abs(rm.out - refm[:, :, 0]).max() < 1e-12
 
 
+def _random_block_set(rng, B, Hq, nqt, nkt, density):
+    """Random block set with the cases that matter forced in: tile 0 left out of
+    some query tiles, and one query tile with an empty set."""
+    sel = rng.random((B, Hq, nqt, nkt)) < density
+    sel[..., 0, 0] = False
+    if nqt > 1:
+        sel[0, 0, 1] = False
+    return sel.astype(np.uint8)
+
+
+def _block_pairs(sel_row, causal, br, bc, Nq, Nk):
+    """[Nq, Nk] booleans: causal visibility and block-set membership, from scratch."""
+    r = np.arange(Nq)[:, None]
+    c = np.arange(Nk)[None, :]
+    ok = np.asarray(sel_row, dtype=bool)[r // br, c // bc]
+    if causal:
+        ok = ok & (c <= r + Nk - Nq)
+    return ok
+
+
+def pin_block_sparse_sdpa(orc):
+    """lambda = 0 inside a block set: softmax attention over the set's keys
+    (torch float64 with the block mask), zero rows and lse -inf where a row
+    sees no key, and every block outside the set reported not visited."""
+    rng = np.random.default_rng(12)
+    for (B, Hq, Hkv, Nq, Nk, d, br, bc, causal) in [
+        (1, 2, 1, 40, 70, 8, 8, 8, True), (2, 2, 2, 33, 50, 4, 5, 7, False),
+        (1, 3, 1, 20, 20, 4, 4, 4, True),
+    ]:
+        q, k, v = _rand_case(rng, B, Hq, Hkv, Nq, Nk, d, d, plant=4.0)
+        nqt, nkt = -(-Nq // br), -(-Nk // bc)
+        sel = _random_block_set(rng, B, Hq, nqt, nkt, 0.5)
+        sc = 1.0 / math.sqrt(d)
+        r = orc.prefill_masked(q, k, v, sel, 0.0, causal, br, bc)
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                ok = _block_pairs(sel[b, h], causal, br, bc, Nq, Nk)
+                seen = ok.any(axis=1)
+                assert (r.out[b, h][~seen] == 0).all() and (r.lse[b, h][~seen] == -np.inf).all()
+                ref = _sdpa(q[b, h][seen][None], k[b, h // G][None], v[b, h // G][None], False, sc,
+                            attn_mask=ok[seen][None])[0]
+                assert np.abs(r.out[b, h][seen] - ref).max() < 1e-12
+                s = sc * q[b, h][seen] @ k[b, h // G].T
+                s = np.where(ok[seen], s, -np.inf)
+                mx = s.max(axis=1)
+                lse = mx + np.log(np.exp(s - mx[:, None]).sum(axis=1))
+                assert np.abs(r.lse[b, h][seen] - lse).max() < 1e-12
+                # visited = in the set and with at least one causally visible pair
+                for i in range(nqt):
+                    for j in range(nkt):
+                        blk = ok[i * br:(i + 1) * br, j * bc:(j + 1) * bc]
+                        assert (r.mask[b, h, i, j] == 2) == (not blk.any())
+        assert (r.mask == 1).sum() == (r.mask != 2).sum(), "lambda 0 drops nothing"
+        assert (r.stats[..., 0] == (r.mask != 2).sum(axis=(2, 3))).all()
+
+
+def pin_block_sparse_kept(orc):
+    """lambda > 0 inside a block set: the output is softmax attention over the
+    set's blocks that the returned mask keeps, and the first tile of the set
+    that a query tile visits is kept."""
+    rng = np.random.default_rng(13)
+    n_dropped = 0
+    for (B, Hq, Hkv, Nq, Nk, d, br, bc, causal, lam) in [
+        (1, 2, 1, 64, 96, 8, 8, 4, True, 1e-2), (1, 2, 2, 30, 80, 8, 6, 5, False, 1e-1),
+    ]:
+        q, k, v = _rand_case(rng, B, Hq, Hkv, Nq, Nk, d, d, plant=6.0)
+        nqt, nkt = -(-Nq // br), -(-Nk // bc)
+        sel = _random_block_set(rng, B, Hq, nqt, nkt, 0.7)
+        sc = 1.0 / math.sqrt(d)
+        r = orc.prefill_masked(q, k, v, sel, lam, causal, br, bc)
+        n_dropped += int((r.mask == 0).sum())
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                assert (r.mask[b, h][sel[b, h] == 0] == 2).all()
+                for i in range(nqt):
+                    vis_t = np.nonzero(r.mask[b, h, i] != 2)[0]
+                    if len(vis_t):
+                        assert r.mask[b, h, i, vis_t[0]] == 1
+                keep = orc.expand_tile_mask(r.mask[b, h], br, bc, Nq, Nk)
+                ok = _block_pairs(sel[b, h], causal, br, bc, Nq, Nk) & keep
+                seen = ok.any(axis=1)
+                ref = _sdpa(q[b, h][seen][None], k[b, h // G][None], v[b, h // G][None], False, sc,
+                            attn_mask=ok[seen][None])[0]
+                assert np.abs(r.out[b, h][seen] - ref).max() < 1e-12
+    assert n_dropped > 0, "fixture must exercise dropped tiles"
+
+
+def pin_block_sparse_full_set(orc):
+    """A block set that holds every block gives the plain skip-softmax prefill."""
+    rng = np.random.default_rng(14)
+    q, k, v = _rand_case(rng, 1, 2, 1, 45, 60, 8, 8, plant=6.0)
+    sel = np.ones((1, 1, 6, 8), dtype=np.uint8)  # broadcast over heads
+    for lam in (0.0, 1e-2):
+        rp = orc.prefill(q, k, v, lam, True, 8, 8)
+        rm = orc.prefill_masked(q, k, v, sel, lam, True, 8, 8)
+        assert np.array_equal(rp.mask, rm.mask)
+        assert np.abs(rp.out - rm.out).max() == 0 and np.abs(rp.lse - rm.lse).max() == 0
+
+
+def pin_block_sparse_brute(orc):
+    rng = np.random.default_rng(15)
+    for trial in range(24):
+        Nq = int(rng.integers(1, 11))
+        Nk = int(rng.integers(Nq, 15))
+        d = int(rng.choice([1, 2, 4]))
+        br = int(rng.choice([1, 2, 3]))
+        bc = int(rng.choice([1, 2, 4]))
+        causal = bool(rng.integers(0, 2))
+        lam = float(rng.choice([0.0, 1e-3, 0.05, 0.3, 1.0]))
+        q, k, v = _rand_case(rng, 1, 1, 1, Nq, Nk, d, 2, plant=float(rng.choice([0.0, 3.0])))
+        nqt, nkt = -(-Nq // br), -(-Nk // bc)
+        sel = (rng.random((nqt, nkt)) < 0.6).astype(np.uint8)
+        sc = 1.0 / math.sqrt(d)
+        r = orc.prefill_masked(q, k, v, sel, lam, causal, br, bc)
+        bm, bo, bl = _brute(q[0, 0].tolist(), k[0, 0].tolist(), v[0, 0].tolist(), lam, causal, br,
+                            bc, sc, sel=sel.tolist())
+        assert r.mask[0, 0].tolist() == bm, trial
+        assert np.abs(r.out[0, 0] - np.array(bo)).max() < 1e-12, trial
+        assert np.array_equal(r.lse[0, 0] == -np.inf, np.array(bl) == -np.inf), trial
+        fin = np.isfinite(np.array(bl))
+        assert np.abs(r.lse[0, 0][fin] - np.array(bl)[fin]).max(initial=0) < 1e-12, trial
+        assert r.stats[0, 0].tolist() == [int((r.mask[0, 0] != 2).sum()), int((r.mask[0, 0] == 1).sum())]
+
+
 PINS = [pin_hand_example, pin_row_aggregation, pin_tie, pin_causal_visibility,
         pin_lambda0_sdpa, pin_bottom_right_causal, pin_masked_sdpa, pin_closed_form_mask,
-        pin_brute_force, pin_decode_sdpa]
+        pin_brute_force, pin_decode_sdpa, pin_block_sparse_sdpa, pin_block_sparse_kept,
+        pin_block_sparse_full_set, pin_block_sparse_brute]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -411,6 +549,13 @@ MUTATIONS = {
     "running_max_not_updated": ("        m = m_new\n", "        m = np.maximum(m, 0 * m_new)\n"),
     "first_tile_not_forced": ("keep = (j == 0) or not (g < thr)", "keep = not (g < thr) and j >= 0"),
     "threshold_log10": ("math.log(lam)", "math.log10(lam)"),
+    "block_set_ignored": ("vis = visible(nq, nk, causal, r0, r1 - r0) & in_set[None, :]",
+                          "vis = visible(nq, nk, causal, r0, r1 - r0)"),
+    "block_set_wrong_query_tile": ("np.repeat(sel[b, hq, i], bc)[:nk]",
+                                   "np.repeat(sel[b, hq, 0], bc)[:nk]"),
+    "block_set_expanded_by_br": ("np.repeat(sel[b, hq, i], bc)[:nk]",
+                                 "np.repeat(sel[b, hq, i], br)[:nk]"),
+    "empty_rows_not_zeroed": ("np.where(seen[:, None], r.out, 0.0)", "r.out"),
 }
 
 

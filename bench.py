@@ -22,6 +22,11 @@ inputs already resident in HBM. The line printed on stdout carries:
                specified, nothing is dropped) and at the supplementary gain 6
                (planted boosts scaled so tiles are dropped): TFLOP/s, skip
                fraction and speed-up over lambda = 0
+  block_sparse_prefill
+               the same layer restricted to seeded block sets shaped like those of
+               block-sparse prefill methods (sink tile, local window, vertical
+               columns, scattered blocks) at densities 0.1 and 0.25: algorithmic
+               TFLOP/s of the selected work and speed-up over dense lambda = 0
   decode       the batch-32 GQA decode over 65536 keys and the batch-16 MLA
                decode over 32768 latent keys: GB/s of the bytes actually read
                (K always, V only for tiles some head keeps) against 8 TB/s
@@ -70,8 +75,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-masked", action="store_true", help="skip the block-sparse prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
-    ap.add_argument("--only", choices=["prefill", "decode_gqa", "decode_mla", "copy"],
+    ap.add_argument("--only", choices=["prefill", "prefill_masked", "decode_gqa", "decode_mla", "copy"],
                     help="launch only this kernel --steps times (for rocprofv3 counter passes)")
     return ap.parse_args()
 
@@ -181,6 +187,45 @@ def bench_prefill(args):
     return out, w
 
 
+def bench_prefill_masked(args, dense_ms):
+    """Block-sparse prefill on the same layer: CRISP-shaped block sets (sink tile,
+    a 2-tile local window at the diagonal, per-head vertical columns and scattered
+    blocks) of two densities, at lambda 0 and the headline lambda. Reports the
+    algorithmic TFLOP/s of the selected work against the MFMA peak and the
+    speed-up over the dense causal call at lambda 0."""
+    import torch
+    from block_sparse_long_skip_amd import attention as A
+    from block_sparse_long_skip_amd import synth
+
+    w = synth.WORKLOADS[2]
+    rows = []
+    for gain in (1.0, 6.0):
+        log(f"[bench] generating {w.name} gain {gain} for block-sparse prefill")
+        inp = synth.make_inputs(w.with_gain(gain))
+        q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+        del inp
+        for density in (0.1, 0.25):
+            bm = torch.from_numpy(synth.block_set(w, density, seed=3)).cuda()
+            for lam in (0.0, args.lam):
+                ms, _, r = time_calls(lambda: A.prefill_masked(q, k, v, bm, lam, causal=True,
+                                                               br=w.br, bc=w.bc),
+                                      max(3, args.steps // 2), 1)
+                alg, visited, kept = prefill_algorithmic_flops(w, r.stats)
+                tf = alg / (ms * 1e-3) / 1e12
+                rows.append(dict(gain=gain, density=density, lam=lam, ms=round(ms, 4),
+                                 algorithmic_tflops=round(tf, 2),
+                                 frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4),
+                                 visited_tiles=int(visited), kept_tiles=int(kept),
+                                 skip_fraction=round(r.skip_fraction, 4),
+                                 speedup_vs_dense_lam0=round(dense_ms / ms, 3)))
+                log(f"[bench]   masked gain {gain} density {density} lam {lam}: {ms:.3f} ms "
+                    f"{tf:.0f} TFLOP/s, visited {int(visited)} kept {int(kept)}")
+            del bm
+        del q, k, v
+        torch.cuda.empty_cache()
+    return rows
+
+
 def bench_decode(args):
     import torch
     from block_sparse_long_skip_amd import attention as A
@@ -286,7 +331,7 @@ def only(args):
         torch.cuda.synchronize()
         log(f"[bench] copied {n} bytes x {args.steps}")
         return
-    cid = {"prefill": 2, "decode_gqa": 3, "decode_mla": 5}[args.only]
+    cid = {"prefill": 2, "prefill_masked": 2, "decode_gqa": 3, "decode_mla": 5}[args.only]
     w = synth.WORKLOADS[cid]
     inp = synth.make_inputs(w)
     q, k = to_device(inp.q, w), to_device(inp.k, w)
@@ -296,8 +341,11 @@ def only(args):
         nws = A.decode_workspace_size(w.B, w.Hq, w.Hkv, w.Nk, w.d, w.dv, latent=v is None,
                                       bc=w.bc)
         ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    bm = torch.from_numpy(synth.block_set(w, 0.1, seed=3)).cuda() if args.only == "prefill_masked" else None
     for _ in range(args.steps):
-        if w.kind == "prefill":
+        if bm is not None:
+            A.prefill_masked(q, k, v, bm, args.lam, causal=True, br=w.br, bc=w.bc, want_stats=False)
+        elif w.kind == "prefill":
             A.prefill(q, k, v, args.lam, causal=True, br=w.br, bc=w.bc, want_stats=False)
         else:
             A.decode(q, k, v, args.lam, bc=w.bc, dv=w.dv, want_stats=False, workspace=ws)
@@ -321,6 +369,8 @@ def main():
         return
     t_start = time.perf_counter()
     pre, w = bench_prefill(args)
+    dense_ms = next((x["ms"] for x in pre["sweep"] if x["gain"] == 1.0 and x["lam"] == 0.0), None)
+    masked = None if args.no_masked or dense_ms is None else bench_prefill_masked(args, dense_ms)
     decode = None if args.no_decode else bench_decode(args)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, w)
     line = {
@@ -342,6 +392,7 @@ def main():
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "lambda_sweep": pre["sweep"],
+        "block_sparse_prefill": masked,
         "decode": decode,
         "wall_s": round(time.perf_counter() - t_start, 1),
     }

@@ -29,8 +29,9 @@ STATUS = {
 }
 
 # Every symbol include/blasst.h declares.
-EXPORTED = ("blasst_attn_prefill", "blasst_attn_decode", "blasst_decode_workspace_size",
-            "blasst_status_string", "blasst_last_error", "blasst_version")
+EXPORTED = ("blasst_attn_prefill", "blasst_attn_prefill_masked", "blasst_attn_decode",
+            "blasst_decode_workspace_size", "blasst_status_string", "blasst_last_error",
+            "blasst_version")
 
 
 class Shape(ctypes.Structure):
@@ -70,6 +71,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                         ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                         ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                         vp]
+    lib.blasst_attn_prefill_masked.restype = ctypes.c_int
+    lib.blasst_attn_prefill_masked.argtypes = [vp, vp, vp, u8p, ctypes.POINTER(ctypes.c_int64), vp,
+                                               u8p, fp, i64p, ctypes.POINTER(Shape),
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                               ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, vp]
     lib.blasst_attn_decode.restype = ctypes.c_int
     lib.blasst_attn_decode.argtypes = [vp, vp, vp, vp, u8p, fp, i64p, ctypes.POINTER(Shape),
                                        ctypes.c_int, ctypes.c_int, ctypes.c_float,
@@ -169,6 +176,43 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: float, causa
     return AttnResult(out, mask, lse, stats)
 
 
+def prefill_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask: torch.Tensor,
+                   lam: float, causal: bool = True, br: int = 128, bc: int = 64,
+                   scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                   out_dtype: Optional[torch.dtype] = None, want_mask: bool = True,
+                   want_lse: bool = True, want_stats: bool = True) -> AttnResult:
+    """Block-sparse skip-softmax prefill: attention restricted to the blocks that
+    ``block_mask`` (bool or uint8, broadcastable to [B, Hq, ceil(Nq/br),
+    ceil(Nk/bc)], on the GPU) marks; the skip rule runs inside the set."""
+    lib = load_library()
+    _require_device(q, k, v, out, block_mask)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk, dv = k.shape[1], k.shape[2], v.shape[3]
+    dev = q.device
+    nqt, nkt = -(-Nq // br), -(-Nk // bc)
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    if block_mask.dtype != torch.uint8:
+        raise TypeError("block_mask must be bool or uint8")
+    bm = block_mask.expand(B, Hq, nqt, nkt)
+    if bm.stride(3) != 1:
+        bm = bm.contiguous()
+    if out is None:
+        out = torch.empty((B, Hq, Nq, dv), dtype=out_dtype or q.dtype, device=dev)
+    mask = torch.empty((B, Hq, nqt, nkt), dtype=torch.uint8, device=dev) if want_mask else None
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev) if want_lse else None
+    stats = torch.empty((B, Hq, 2), dtype=torch.int64, device=dev) if want_stats else None
+    sh = Shape(B, Hq, Hkv, Nq, Nk, d, dv, _strides3(q), _strides3(k), _strides3(v), _strides3(out))
+    bms = (ctypes.c_int64 * 3)(bm.stride(0), bm.stride(1), bm.stride(2))
+    st = lib.blasst_attn_prefill_masked(_ptr(q), _ptr(k), _ptr(v), _ptr(bm), bms, _ptr(out),
+                                        _ptr(mask), _ptr(lse), _ptr(stats), ctypes.byref(sh),
+                                        _dtype_code(q.dtype), _dtype_code(out.dtype), float(lam),
+                                        float(scale) if scale else 0.0, int(bool(causal)),
+                                        int(br), int(bc), _stream(dev))
+    _check(st)
+    return AttnResult(out, mask, lse, stats)
+
+
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], lam: float,
            bc: int = 64, scale: Optional[float] = None, dv: Optional[int] = None,
            out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
@@ -238,5 +282,5 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
-__all__ = ["prefill", "decode", "decode_workspace_size", "load_library", "Shape", "BlasstError", "AttnResult",
+__all__ = ["prefill", "prefill_masked", "decode", "decode_workspace_size", "load_library", "Shape", "BlasstError", "AttnResult",
            "EXPORTED", "LIB_PATH", "STATUS"]

@@ -88,35 +88,13 @@ blasst_status_t zero_stats(int64_t* stats, int64_t n, hipStream_t st) {
   return BLASST_OK;
 }
 
-}  // namespace
-
-extern "C" {
-
-int blasst_version(void) { return BLASST_VERSION; }
-
-const char* blasst_last_error(void) { return g_last_error; }
-
-const char* blasst_status_string(blasst_status_t s) {
-  switch (s) {
-    case BLASST_OK: return "BLASST_OK";
-    case BLASST_E_NULL: return "BLASST_E_NULL: a required pointer is NULL";
-    case BLASST_E_SHAPE: return "BLASST_E_SHAPE: invalid sizes";
-    case BLASST_E_DTYPE: return "BLASST_E_DTYPE: unknown dtype";
-    case BLASST_E_LAMBDA: return "BLASST_E_LAMBDA: lambda outside [0, 1] or NaN";
-    case BLASST_E_ALIGN: return "BLASST_E_ALIGN: pointer or stride not 16-byte aligned";
-    case BLASST_E_UNSUPPORTED: return "BLASST_E_UNSUPPORTED: no kernel for this combination";
-    case BLASST_E_ARG: return "BLASST_E_ARG: invalid scalar argument";
-    case BLASST_E_HIP: return "BLASST_E_HIP: HIP runtime error";
-    case BLASST_E_WORKSPACE: return "BLASST_E_WORKSPACE: workspace missing, too small or misaligned";
-  }
-  return "BLASST: unknown status";
-}
-
-blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v, void* out,
-                                    uint8_t* mask_out, float* lse_out, int64_t* stats_out,
-                                    const blasst_shape_t* shape, blasst_dtype_t dtype,
-                                    blasst_dtype_t out_dtype, float lambda, float scale,
-                                    int causal, int br, int bc, void* stream) {
+// Both prefill entry points; block_mask is NULL for plain prefill.
+blasst_status_t run_prefill(const void* q, const void* k, const void* v,
+                            const uint8_t* block_mask, const int64_t* block_mask_stride,
+                            void* out, uint8_t* mask_out, float* lse_out, int64_t* stats_out,
+                            const blasst_shape_t* shape, blasst_dtype_t dtype,
+                            blasst_dtype_t out_dtype, float lambda, float scale, int causal,
+                            int br, int bc, void* stream) {
   blasst_status_t st0;
   if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
   if (!q || !k || !v || !out) return fail(BLASST_E_NULL, "q, k, v and out are required");
@@ -159,11 +137,24 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
   const int64_t nkt = ((int64_t)s.len_kv + bc - 1) / bc;
   if ((int64_t)s.batch * s.heads_q * nqt > 0x7fffffffLL)
     return fail(BLASST_E_UNSUPPORTED, "grid too large");
+  if (block_mask) {
+    if (!b16)
+      return fail(BLASST_E_UNSUPPORTED, "block-sparse prefill needs bf16 inputs, d = 128, 128x64 tiles");
+    if (block_mask_stride[0] < 0 || block_mask_stride[1] < 0 || block_mask_stride[2] < 0)
+      return fail(BLASST_E_SHAPE, "block_mask strides must be >= 0");
+    if (nkt > blasst::kPrefillMaxSetTiles)
+      return fail(BLASST_E_UNSUPPORTED, "block-sparse prefill supports at most %d key tiles (got %lld)",
+                  blasst::kPrefillMaxSetTiles, (long long)nkt);
+  }
 
   const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)s.d_qk));
   blasst::PrefillArgs a;
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.mask = mask_out; a.lse = lse_out; a.stats = stats_out;
+  a.block_mask = block_mask;
+  a.bms0 = block_mask ? block_mask_stride[0] : 0;
+  a.bms1 = block_mask ? block_mask_stride[1] : 0;
+  a.bms2 = block_mask ? block_mask_stride[2] : 0;
   a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nq = s.len_q; a.Nk = s.len_kv;
   a.nqt = (int)nqt; a.nkt = (int)nkt; a.causal = causal ? 1 : 0;
   a.out_f32 = out_dtype == BLASST_FP32 ? 1 : 0;
@@ -181,6 +172,53 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
   if (s.batch == 0 || s.len_q == 0) return ok();
   const hipError_t e = f32 ? blasst::launch_prefill_f32(a, hs) : blasst::launch_prefill_bf16(a, hs);
   return hip_status(e, "prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+int blasst_version(void) { return BLASST_VERSION; }
+
+const char* blasst_last_error(void) { return g_last_error; }
+
+const char* blasst_status_string(blasst_status_t s) {
+  switch (s) {
+    case BLASST_OK: return "BLASST_OK";
+    case BLASST_E_NULL: return "BLASST_E_NULL: a required pointer is NULL";
+    case BLASST_E_SHAPE: return "BLASST_E_SHAPE: invalid sizes";
+    case BLASST_E_DTYPE: return "BLASST_E_DTYPE: unknown dtype";
+    case BLASST_E_LAMBDA: return "BLASST_E_LAMBDA: lambda outside [0, 1] or NaN";
+    case BLASST_E_ALIGN: return "BLASST_E_ALIGN: pointer or stride not 16-byte aligned";
+    case BLASST_E_UNSUPPORTED: return "BLASST_E_UNSUPPORTED: no kernel for this combination";
+    case BLASST_E_ARG: return "BLASST_E_ARG: invalid scalar argument";
+    case BLASST_E_HIP: return "BLASST_E_HIP: HIP runtime error";
+    case BLASST_E_WORKSPACE: return "BLASST_E_WORKSPACE: workspace missing, too small or misaligned";
+  }
+  return "BLASST: unknown status";
+}
+
+blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v, void* out,
+                                    uint8_t* mask_out, float* lse_out, int64_t* stats_out,
+                                    const blasst_shape_t* shape, blasst_dtype_t dtype,
+                                    blasst_dtype_t out_dtype, float lambda, float scale,
+                                    int causal, int br, int bc, void* stream) {
+  return run_prefill(q, k, v, nullptr, nullptr, out, mask_out, lse_out, stats_out, shape, dtype,
+                     out_dtype, lambda, scale, causal, br, bc, stream);
+}
+
+blasst_status_t blasst_attn_prefill_masked(const void* q, const void* k, const void* v,
+                                           const uint8_t* block_mask,
+                                           const int64_t block_mask_stride[3], void* out,
+                                           uint8_t* mask_out, float* lse_out,
+                                           int64_t* stats_out, const blasst_shape_t* shape,
+                                           blasst_dtype_t dtype, blasst_dtype_t out_dtype,
+                                           float lambda, float scale, int causal, int br, int bc,
+                                           void* stream) {
+  if (!block_mask || !block_mask_stride)
+    return fail(BLASST_E_NULL, "block_mask and block_mask_stride are required");
+  return run_prefill(q, k, v, block_mask, block_mask_stride, out, mask_out, lse_out, stats_out,
+                     shape, dtype, out_dtype, lambda, scale, causal, br, bc, stream);
 }
 
 }  // extern "C"

@@ -16,6 +16,10 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kNegInf = -__builtin_inff();
 
+// Longest block-set row (key tiles of one query tile) the block-sparse prefill
+// lists in LDS.
+constexpr int kPrefillMaxSetTiles = 6144;
+
 // Arguments of every prefill kernel (element strides; last dim contiguous).
 struct PrefillArgs {
   const void* q;
@@ -25,6 +29,10 @@ struct PrefillArgs {
   uint8_t* mask;   // nullable [B,Hq,nqt,nkt]
   float* lse;      // nullable [B,Hq,Nq]
   int64_t* stats;  // nullable [B,Hq,2], zeroed by the launcher
+  // nullable block set [B,Hq,nqt,nkt] (element strides bms0..bms2, key tiles
+  // contiguous; a zero stride broadcasts): nonzero = the block may be attended
+  const uint8_t* block_mask;
+  int64_t bms0, bms1, bms2;
   int B, Hq, Hkv, Nq, Nk;
   int nqt, nkt;
   int causal;

@@ -44,6 +44,14 @@
 // (no register staging): a buffer resource per tile (uniform base and range),
 // a per-lane 32-bit offset fixed for the whole loop, and no vector ALU work
 // per copy. LDS reads are a per-lane base plus immediate offsets.
+//
+// Block-sparse mode (the MASKED instance): attention is restricted to a
+// caller-given set of (query tile, key tile) blocks, as in the final stage of
+// block-sparse prefill methods, which compute ordinary softmax attention inside
+// the selected blocks (CRISP summary on rit.work, section "Что сделали"). The
+// workgroup first lists its row of the set in LDS, in increasing key order;
+// the pipeline above then walks that list instead of [0, J), so tiles outside
+// the set cost nothing and the skip rule runs over the set's tiles only.
 #include <type_traits>
 
 #include "common.hpp"
@@ -72,10 +80,15 @@ struct RowState {
 
 }  // namespace
 
+// MASKED: block-sparse mode. The query tile visits only the key tiles of its
+// row of the block set, in increasing order, from a list built in LDS.
+template <bool MASKED>
 __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char Ks[2][TILE_BYTES];
   __shared__ __attribute__((aligned(16))) char Vs[2][TILE_BYTES];
   __shared__ int votes[2][4];
+  __shared__ uint16_t tlist[MASKED ? kPrefillMaxSetTiles : 1];
+  __shared__ int wcount[4];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -275,29 +288,55 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   int kept = 0;
   uint8_t* mrow = a.mask ? a.mask + ((int64_t)bh * a.nqt + i) * a.nkt : nullptr;
 
-  // ---- prologue: K_0, K_1 and V_0 (tile 0 is always kept) into LDS, then S_0
-  tile_to_lds(Ks[0], kp, koff, a.ks2, 0);
-  if (J > 1) tile_to_lds(Ks[1], kp, koff, a.ks2, BC);
-  tile_to_lds(Vs[0], vp, voff, a.vs2, 0);
-  wait_vmem();
-  __syncthreads();
-  f32x16_t sA[2], sB[2];
-  scores(Ks[0], sA);
-  if (tile_needs_mask(0)) mask_scores(0, sA);
-  float mt = rowmax(sA);
-  bool keep = true;
-  if (mrow && t == 0) mrow[0] = 1;
-  __syncthreads();  // every wave has read K_0 before it is overwritten
+  // The n key tiles this query tile visits: [0, J), or in block-sparse mode
+  // the set's tiles among them, listed in increasing order. The list is built
+  // from per-thread runs of consecutive tiles and a prefix sum of the run
+  // counts; blocks outside the set get mask 2 here.
+  int n = J;
+  if constexpr (MASKED) {
+    const uint8_t* sel = a.block_mask + b * a.bms0 + hq * a.bms1 + (int64_t)i * a.bms2;
+    const int per = (J + NT - 1) / NT;
+    const int x0 = min(t * per, J), x1 = min(x0 + per, J);
+    int cnt = 0;
+    for (int x = x0; x < x1; ++x) cnt += sel[x] != 0;
+    int incl = cnt;  // inclusive prefix sum over the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += y;
+    }
+    if (lane == 63) wcount[w] = incl;
+    __syncthreads();
+    int pos = incl - cnt;
+    for (int ww = 0; ww < w; ++ww) pos += wcount[ww];
+    n = __builtin_amdgcn_readfirstlane(wcount[0] + wcount[1] + wcount[2] + wcount[3]);
+    for (int x = x0; x < x1; ++x) {
+      if (sel[x]) tlist[pos++] = (uint16_t)x;
+      else if (mrow) mrow[x] = 2;
+    }
+    if (mrow)
+      for (int x = J + t; x < a.nkt; x += NT) mrow[x] = 2;
+    __syncthreads();
+  }
+  // key-tile index of the x-th visited tile (uniform)
+  auto tile_at = [&](int x) -> int {
+    if constexpr (MASKED) return __builtin_amdgcn_readfirstlane((int)tlist[x]);
+    else return x;
+  };
 
+  f32x16_t sA[2], sB[2];
+  float mt = kNegInf;
+  bool keep = true;
   int j = 0;
   // one key tile; P = j & 1 (compile-time), s = S_j, sn receives S_{j+1}
   auto step = [&](auto PAR, f32x16_t (&s)[2], f32x16_t (&sn)[2]) {
     constexpr int P = decltype(PAR)::value;
-    const int c0 = j * BC;
-    const bool has_next = j + 1 < J;
+    const int c0 = tile_at(j) * BC;
+    const bool has_next = j + 1 < n;
+    const int cn = has_next ? tile_at(j + 1) * BC : 0;
     // (a) K_{j+2} straight into the buffer K_j used (every wave read it before
     //     the previous barrier)
-    if (j + 2 < J) tile_to_lds(Ks[P], kp, koff, a.ks2, c0 + 2 * BC);
+    if (j + 2 < n) tile_to_lds(Ks[P], kp, koff, a.ks2, tile_at(j + 2) * BC);
     // (b, c) scores of tile j+1 (MFMA) and P_j (VALU)
     st.m_prefix = fmaxf(st.m_prefix, mt);  // running max through tile j
     bf16x8_t pb[4];
@@ -329,7 +368,7 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       for (int c = 0; c < 4; ++c) pb[c] = as_bf16x8((u32x4_t){pw[c][0], pw[c][1], pw[c][2], pw[c][3]});
       st.l += ls0 + ls1;
     }
-    if (has_next && tile_needs_mask(c0 + BC)) mask_scores(c0 + BC, sn);
+    if (has_next && tile_needs_mask(cn)) mask_scores(cn, sn);
     // (e) vote on tile j+1 against the running max through tile j
     float mtn = kNegInf;
     if (has_next) {
@@ -344,10 +383,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     if (has_next) {
       const int* vv = votes[P ^ 1];
       keep_next = (vv[0] | vv[1] | vv[2] | vv[3]) != 0;
-      if (mrow && t == 0) mrow[j + 1] = keep_next ? 1 : 0;
+      if (mrow && t == 0) mrow[cn / BC] = keep_next ? 1 : 0;
       // (h) V_{j+1} is fetched only for a kept tile, into the buffer V_{j-1}
       //     used (every wave finished reading it before this barrier)
-      if (keep_next) tile_to_lds(Vs[P ^ 1], vp, voff, a.vs2, c0 + BC);
+      if (keep_next) tile_to_lds(Vs[P ^ 1], vp, voff, a.vs2, cn);
     }
     // (i) O^T += V_j^T P_j^T: per key chunk c, the 4 output blocks are
     //     independent MFMA chains; the next chunk's V^T reads are issued first
@@ -382,30 +421,50 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   };
   const std::integral_constant<int, 0> even;
   const std::integral_constant<int, 1> odd;
-  while (j < J) {
-    step(even, sA, sB);
-    if (j >= J) break;
-    step(odd, sB, sA);
+  if (n > 0) {
+    // ---- prologue: K_0, K_1 and V_0 (the first visited tile is always kept)
+    //      into LDS, then S_0
+    const int c0 = tile_at(0) * BC;
+    tile_to_lds(Ks[0], kp, koff, a.ks2, c0);
+    if (n > 1) tile_to_lds(Ks[1], kp, koff, a.ks2, tile_at(1) * BC);
+    tile_to_lds(Vs[0], vp, voff, a.vs2, c0);
+    wait_vmem();
+    __syncthreads();
+    scores(Ks[0], sA);
+    if (tile_needs_mask(c0)) mask_scores(c0, sA);
+    mt = rowmax(sA);
+    if (mrow && t == 0) mrow[c0 / BC] = 1;
+    __syncthreads();  // every wave has read K_0 before it is overwritten
+    while (j < n) {
+      step(even, sA, sB);
+      if (j >= n) break;
+      step(odd, sB, sA);
+    }
   }
-  if (mrow) {
+  if (!MASKED && mrow) {
     for (int x = J + t; x < a.nkt; x += NT) mrow[x] = 2;
   }
 
-  // epilogue: this lane and lane ^ 32 hold partial sums of the same row
+  // epilogue: this lane and lane ^ 32 hold partial sums of the same row. In
+  // block-sparse mode a row may see no key at all (its running max is still
+  // -inf and its sums are not meaningful): it outputs zero and lse -inf.
   const float lt = sum_with_lane_xor32(st.l);
   if (valid) {
-    const float inv = 1.f / lt;
+    const bool seen = !MASKED || st.m_prefix != kNegInf;
+    const float inv = seen ? 1.f / lt : 0.f;
+    auto ov = [&](float x) { return seen ? x * inv : 0.f; };
     const int64_t ob = b * a.os0 + hq * a.os1 + (int64_t)row * a.os2;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int qd = 0; qd < 4; ++qd)
-        store_out4(a.out, ob + 32 * db + 8 * qd + 4 * h, a.out_f32, o[db][4 * qd] * inv,
-                   o[db][4 * qd + 1] * inv, o[db][4 * qd + 2] * inv, o[db][4 * qd + 3] * inv);
-    if (a.lse && h == 0) a.lse[(int64_t)bh * a.Nq + row] = st.m_acc * a.scale + logf(lt);
+        store_out4(a.out, ob + 32 * db + 8 * qd + 4 * h, a.out_f32, ov(o[db][4 * qd]),
+                   ov(o[db][4 * qd + 1]), ov(o[db][4 * qd + 2]), ov(o[db][4 * qd + 3]));
+    if (a.lse && h == 0)
+      a.lse[(int64_t)bh * a.Nq + row] = seen ? st.m_acc * a.scale + logf(lt) : kNegInf;
   }
   if (a.stats && t == 0) {
-    atomicAdd((unsigned long long*)&a.stats[2 * bh], (unsigned long long)J);
+    atomicAdd((unsigned long long*)&a.stats[2 * bh], (unsigned long long)n);
     atomicAdd((unsigned long long*)&a.stats[2 * bh + 1], (unsigned long long)kept);
   }
 }
@@ -413,7 +472,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
   const int64_t nblocks = (int64_t)a.B * a.Hq * a.nqt;
   if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(prefill_bf16_kernel, dim3((unsigned)nblocks), dim3(NT), 0, stream, a);
+  if (a.block_mask)
+    hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3((unsigned)nblocks), dim3(NT), 0, stream, a);
+  else
+    hipLaunchKernelGGL(prefill_bf16_kernel<false>, dim3((unsigned)nblocks), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -248,6 +248,35 @@ def small_workload(kind: str = "prefill", *, B=1, Hq=2, Hkv=1, Nq=200, Nk=200, d
                     gain=gain)
 
 
+def block_set(w: Workload, density: float, *, local: int = 2, sink: bool = True,
+              seed: int = 0) -> np.ndarray:
+    """A seeded block set [B, Hq, nQt, nKt] (uint8, 1 = block selected) for
+    block-sparse prefill, shaped like the sets block-sparse prefill methods
+    select (CRISP write-up on rit.work, "Что сделали"): the first key tile
+    (attention sinks) when ``sink``, the ``local`` key tiles ending at each
+    query tile's causal diagonal (recent window), a per-head set of "vertical"
+    key-tile columns selected for every query tile, and scattered blocks. The
+    vertical columns and the scattered blocks each take about ``density / 2``
+    of the tiles. Blocks past the diagonal are drawn too (a kernel must ignore
+    them)."""
+    nqt, nkt = n_tiles(w.Nq, w.br), n_tiles(w.Nk, w.bc)
+    out = np.zeros((w.B, w.Hq, nqt, nkt), dtype=np.uint8)
+    last = (np.minimum((np.arange(nqt) + 1) * w.br, w.Nq) - 1 + (w.Nk - w.Nq if w.causal else 0))
+    diag = np.minimum(last // w.bc, nkt - 1) if w.causal else np.full(nqt, nkt - 1)
+    cols = np.arange(nkt)[None, :]
+    for b in range(w.B):
+        for h in range(w.Hq):
+            rng = _rng(w.seed, 6, seed, b, h)
+            vertical = rng.random(nkt) < density / 2
+            scattered = rng.random((nqt, nkt)) < density / 2
+            sel = vertical[None, :] | scattered
+            sel |= (cols > diag[:, None] - local) & (cols <= diag[:, None])
+            if sink:
+                sel[:, 0] = True
+            out[b, h] = sel
+    return out
+
+
 def dense_equivalent_flops(w: Workload) -> float:
     """2*(d+dv) FLOPs per visible (query, key) pair, summed over batch and heads."""
     if w.kind == "prefill" and w.causal:
@@ -266,7 +295,7 @@ def n_tiles(n: int, t: int) -> int:
 __all__ = [
     "Workload", "WORKLOADS", "Inputs", "make_inputs", "small_workload", "q_slice", "k_slice",
     "v_slice", "unit_direction", "needle_positions", "needle_rates", "f32_to_bf16_bits",
-    "bf16_bits_to_f32", "to_float", "dense_equivalent_flops", "n_tiles",
+    "bf16_bits_to_f32", "to_float", "dense_equivalent_flops", "n_tiles", "block_set",
 ]
 
 

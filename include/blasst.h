@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define BLASST_VERSION 200 /* 2.0.0: decode takes a workspace */
+#define BLASST_VERSION 210 /* 2.1.0: block-sparse prefill */
 
 typedef enum blasst_status {
   BLASST_OK = 0,
@@ -106,7 +106,8 @@ typedef struct blasst_shape {
 /* Mask values written to mask_out. */
 #define BLASST_TILE_DROPPED 0
 #define BLASST_TILE_KEPT 1
-#define BLASST_TILE_NOT_VISITED 2 /* causally empty: no visible (row, key) pair */
+#define BLASST_TILE_NOT_VISITED 2 /* no visible (row, key) pair: causally empty, or
+                                     outside the block set in block-sparse mode */
 
 /*
  * Prefill: out = skip-softmax attention of q against k, v.
@@ -131,6 +132,44 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
                                     const blasst_shape_t* shape, blasst_dtype_t dtype,
                                     blasst_dtype_t out_dtype, float lambda, float scale,
                                     int causal, int br, int bc, void* stream);
+
+/*
+ * Block-sparse prefill: blasst_attn_prefill restricted to a caller-given set
+ * of (query tile, key tile) blocks. Plain softmax attention computed inside a
+ * selected block set is the final stage of block-sparse prefill methods (the
+ * CRISP summary on rit.work, section "Что сделали"); block-sparse masks are
+ * one of the mask kinds of the LongCA-bench post on denisavetisyan.com
+ * (section "Сад Внимания: LongCA-bench и Стандартизация Оценки").
+ *
+ *   block_mask         DEVICE uint8 [B, Hq, ceil(Nq/br), ceil(Nk/bc)], owned
+ *                      by the caller, read only: nonzero marks a block the
+ *                      query tile may attend
+ *   block_mask_stride  HOST int64[3]: element strides of block_mask's batch,
+ *                      head and query-tile dimensions (>= 0; 0 broadcasts one
+ *                      set over that dimension); key tiles are contiguous
+ *   everything else    as for blasst_attn_prefill
+ *
+ * A (query, key) pair is visible when the causal rule allows it and its block
+ * is in the set. The skip rule runs over the set's key tiles only, in
+ * increasing order: the first of them that a query tile visits is always
+ * kept, and the running max covers kept tiles of the set. Blocks outside the
+ * set are reported BLASST_TILE_NOT_VISITED and never read. A query row that
+ * sees no key at all gets a zero output row and lse -inf. With every block in
+ * the set the result equals blasst_attn_prefill's.
+ *
+ * Supported (else BLASST_E_UNSUPPORTED): BLASST_BF16, d_qk = d_v = 128,
+ * br = 128, bc = 64, ceil(Nk/64) <= 6144 (Nk <= 393216).
+ * NULL block_mask or block_mask_stride is BLASST_E_NULL; a negative stride is
+ * BLASST_E_SHAPE.
+ */
+blasst_status_t blasst_attn_prefill_masked(const void* q, const void* k, const void* v,
+                                           const uint8_t* block_mask,
+                                           const int64_t block_mask_stride[3], void* out,
+                                           uint8_t* mask_out, float* lse_out,
+                                           int64_t* stats_out, const blasst_shape_t* shape,
+                                           blasst_dtype_t dtype, blasst_dtype_t out_dtype,
+                                           float lambda, float scale, int causal, int br, int bc,
+                                           void* stream);
 
 /*
  * Decode: one query token per (batch, query head) against a contiguous KV

@@ -211,6 +211,30 @@ def prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, lam: float, causal: boo
     return OracleResult(out, lse, mask, gap, stats)
 
 
+def block_sparse_rows(q_rows: np.ndarray, k: np.ndarray, v: np.ndarray, sel_row: np.ndarray,
+                      lam: float, causal: bool, nq: int, row0: int, bc: int,
+                      scale: float) -> TileRowResult:
+    """One query tile of block-sparse prefill against one key/value head.
+
+    q_rows: [rows, d], the queries row0 .. row0+rows-1 of a call with nq
+    queries; k: [Nk, d]; v: [Nk, dv]; sel_row: [nKt], this query tile's row of
+    the block set (nonzero = may attend). A (query, key) pair is visible when
+    the causal rule allows it and its key tile is in the set; the skip rule then
+    runs on that visibility, so tiles outside the set are "not visited" and the
+    first tile of the set that has a visible pair is kept (its rows have no
+    running max yet, so their gap is +inf). A row that sees no key outputs zero
+    with lse = -inf.
+    """
+    nk = k.shape[0]
+    in_set = np.repeat(np.asarray(sel_row) != 0, bc)[:nk]
+    vis = visible(nq, nk, causal, row0, len(q_rows)) & in_set[None, :]
+    r = blasst_rows(q_rows, k, v, lam, bc, vis, scale)
+    seen = vis.any(axis=1)
+    r.out = np.where(seen[:, None], r.out, 0.0)
+    r.lse = np.where(seen, r.lse, -np.inf)
+    return r
+
+
 def prefill_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_mask: np.ndarray,
                    lam: float, causal: bool, br: int, bc: int,
                    scale: Optional[float] = None) -> OracleResult:
@@ -220,16 +244,11 @@ def prefill_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_mask: np.n
     last stage of block-sparse prefill methods (the CRISP summary on rit.work,
     section "Что сделали", last paragraph); block-sparse masks are one of the
     mask kinds of the LongCA-bench post on denisavetisyan.com (section "Сад
-    Внимания: LongCA-bench и Стандартизация Оценки"). The skip rule runs inside
-    the set: the set's key tiles are visited in increasing order, the first one
-    a query tile visits is always kept (its rows have no running max yet, so
-    their gap is +inf), and the running max covers kept tiles of the set only.
+    Внимания: LongCA-bench и Стандартизация Оценки"). Each query tile runs
+    block_sparse_rows on its row of the set.
 
     block_mask: [B, Hq, nQt, nKt], broadcastable from the left; nonzero marks
-    a block the query tile may attend. A (query, key) pair is visible when the
-    causal rule allows it and its block is in the set. Blocks outside the set
-    are "not visited" (mask value 2). A row that sees no key at all gets a zero
-    output and lse = -inf.
+    a block the query tile may attend.
     """
     B, Hq, nq, d = q.shape
     hkv, nk = k.shape[1], k.shape[2]
@@ -241,7 +260,7 @@ def prefill_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_mask: np.n
     if scale is None:
         scale = default_scale(d)
     nqt, nkt = -(-nq // br), -(-nk // bc)
-    sel = np.broadcast_to(np.asarray(block_mask) != 0, (B, Hq, nqt, nkt))
+    sel = np.broadcast_to(np.asarray(block_mask), (B, Hq, nqt, nkt))
     out = np.zeros((B, Hq, nq, dv))
     lse = np.full((B, Hq, nq), -np.inf)
     mask = np.full((B, Hq, nqt, nkt), MASK_NOT_VISITED, dtype=np.uint8)
@@ -252,12 +271,10 @@ def prefill_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_mask: np.n
             kvh = hq // (Hq // hkv)
             for i in range(nqt):
                 r0, r1 = i * br, min((i + 1) * br, nq)
-                in_set = np.repeat(sel[b, hq, i], bc)[:nk]
-                vis = visible(nq, nk, causal, r0, r1 - r0) & in_set[None, :]
-                r = blasst_rows(q[b, hq, r0:r1], k[b, kvh], v[b, kvh], lam, bc, vis, scale)
-                seen = vis.any(axis=1)
-                out[b, hq, r0:r1] = np.where(seen[:, None], r.out, 0.0)
-                lse[b, hq, r0:r1] = np.where(seen, r.lse, -np.inf)
+                r = block_sparse_rows(q[b, hq, r0:r1], k[b, kvh], v[b, kvh], sel[b, hq, i], lam,
+                                      causal, nq, r0, bc, scale)
+                out[b, hq, r0:r1] = r.out
+                lse[b, hq, r0:r1] = r.lse
                 mask[b, hq, i] = r.mask
                 gap[b, hq, i] = r.gap
             stats[b, hq, 0] = int((mask[b, hq] != MASK_NOT_VISITED).sum())
@@ -354,7 +371,7 @@ def masked_dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np
 
 __all__ = [
     "threshold", "default_scale", "visible", "blasst_rows", "prefill_tile", "prefill",
-    "prefill_masked",
+    "block_sparse_rows", "prefill_masked",
     "decode_row", "decode", "naive_attention", "expand_tile_mask", "masked_dense_attention",
     "OracleResult", "TileRowResult", "MASK_SKIPPED", "MASK_KEPT", "MASK_NOT_VISITED",
 ]

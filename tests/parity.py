@@ -52,6 +52,8 @@ class Tally:
     notes: list = field(default_factory=list)
 
     def add(self, err: np.ndarray, lse_err: np.ndarray, ref: np.ndarray):
+        # lse -inf on both sides (a row that sees no key) is a match
+        lse_err = np.where(np.isnan(lse_err), np.inf, lse_err)
         self.abs_err.append(np.abs(err).ravel())
         self.ref_abs.append(np.abs(ref).ravel())
         self.lse_err.append(np.abs(lse_err).ravel())
@@ -86,7 +88,9 @@ def check_mask_row(gpu_row: np.ndarray, orc_row: np.ndarray, gap_row: np.ndarray
     visited = orc_row != oracle.MASK_NOT_VISITED
     assert np.array_equal(gpu_row == oracle.MASK_NOT_VISITED, ~visited), f"{where}: visited set"
     assert set(np.unique(gpu_row)).issubset({0, 1, 2}), f"{where}: mask values"
-    assert gpu_row[0] == oracle.MASK_KEPT, f"{where}: tile 0 must be kept"
+    first = np.nonzero(visited)[0]
+    if len(first):
+        assert gpu_row[first[0]] == oracle.MASK_KEPT, f"{where}: first visited tile must be kept"
     near = visited & (np.abs(gap_row - thr) <= BAND) if math.isfinite(thr) else np.zeros_like(visited)
     tally.band += int(near.sum())
     flips = visited & (gpu_row != orc_row)
@@ -128,6 +132,40 @@ def prefill_tile_parity(res, inp, w: synth.Workload, lam: float, b: int, h: int,
     got = from_device(res.out[b, h, r0:r1])
     got_lse = res.lse[b, h, r0:r1].cpu().numpy().astype(np.float64)
     tally.add(got - ref_out, got_lse - ref_lse, ref_out)
+    return t
+
+
+def lse_diff(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """got - ref, with 0 where both are -inf (NaN where only one is, which fails)."""
+    both = (got == -np.inf) & (ref == -np.inf)
+    with np.errstate(invalid="ignore"):
+        d = got - ref
+    d = np.where(both, 0.0, d)
+    return np.where(np.isinf(d), np.nan, d)
+
+
+def prefill_masked_tile_parity(res, inp, w: synth.Workload, lam: float, sel: np.ndarray, b: int,
+                               h: int, i: int, tally: Tally, kf=None, vf=None):
+    """Compare one (b, h, query tile i) of a GPU block-sparse prefill with the
+    oracle's block_sparse_rows; sel is the block set [B, Hq, nQt, nKt]."""
+    kvh = h // (w.Hq // w.Hkv)
+    r0, r1 = i * w.br, min((i + 1) * w.br, w.Nq)
+    q = synth.to_float(inp.q[b, h, r0:r1], w)
+    k = kf if kf is not None else synth.to_float(inp.k[b, kvh], w)
+    v = vf if vf is not None else synth.to_float(inp.v[b, kvh], w)
+    scale = 1.0 / math.sqrt(w.d)
+    t = oracle.block_sparse_rows(q, k, v, sel[b, h, i], lam, w.causal, w.Nq, r0, w.bc, scale)
+    gpu_mask = res.mask[b, h, i].cpu().numpy()
+    flips = check_mask_row(gpu_mask, t.mask, t.gap, lam, tally, f"b{b} h{h} qtile{i}")
+    ref_out, ref_lse = t.out, t.lse
+    if flips.any():
+        # same routine on the GPU's own kept set: the set narrowed to its kept tiles
+        kept = (gpu_mask == oracle.MASK_KEPT).astype(np.uint8)
+        t2 = oracle.block_sparse_rows(q, k, v, kept, 0.0, w.causal, w.Nq, r0, w.bc, scale)
+        ref_out, ref_lse = t2.out, t2.lse
+    got = from_device(res.out[b, h, r0:r1])
+    got_lse = res.lse[b, h, r0:r1].cpu().numpy().astype(np.float64)
+    tally.add(got - ref_out, lse_diff(got_lse, ref_lse), ref_out)
     return t
 
 

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(A.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.blasst_version() == 200
+    assert lib.blasst_version() == 210
 
 
 def test_status_strings():
@@ -130,6 +130,42 @@ def test_prefill_validation(case, expect):
     elif case == "overlapping_kv_rows":
         sh.k_stride[2] = 64
     assert _prefill(sh, **kw) == expect, _err()
+    assert _err() != ""
+
+
+def _prefill_masked(sh, bm=P, bms=(0, 0, 4), dtype=BF16, br=128, bc=64, lam=1e-3, q=P):
+    lib = A.load_library()
+    strides = None if bms is None else (ctypes.c_int64 * 3)(*bms)
+    return lib.blasst_attn_prefill_masked(q, P, P, bm, strides, P, None, None, None,
+                                          ctypes.byref(sh), dtype, dtype, lam, 0.0, 1, br, bc,
+                                          None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_block_mask", 1), ("null_strides", 1), ("negative_stride", 2), ("f32", 6),
+    ("too_many_key_tiles", 6), ("bad_tile", 6), ("null_q", 1), ("lam", 4),
+])
+def test_prefill_masked_validation(case, expect):
+    sh = _shape()
+    kw = {}
+    if case == "null_block_mask":
+        kw["bm"] = None
+    elif case == "null_strides":
+        kw["bms"] = None
+    elif case == "negative_stride":
+        kw["bms"] = (0, -4, 4)
+    elif case == "f32":
+        sh = _shape(d=64, dv=64)
+        kw["dtype"], kw["br"] = FP32, 64
+    elif case == "too_many_key_tiles":
+        sh = _shape(Nq=128, Nk=6144 * 64 + 1)
+    elif case == "bad_tile":
+        kw["br"] = 64
+    elif case == "null_q":
+        kw["q"] = None
+    elif case == "lam":
+        kw["lam"] = -1.0
+    assert _prefill_masked(sh, **kw) == expect, _err()
     assert _err() != ""
 
 

@@ -17,7 +17,8 @@ import torch
 import oracle
 from block_sparse_long_skip_amd import attention as A
 from block_sparse_long_skip_amd import synth
-from parity import Tally, decode_row_parity, from_device, prefill_tile_parity, sample_qtiles, to_device
+from parity import (Tally, decode_row_parity, from_device, prefill_masked_tile_parity,
+                    prefill_tile_parity, sample_qtiles, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -243,6 +244,129 @@ def test_decode_mla_workspace_reuse():
     r3 = _decode(i1, w1, 1e-2, "fp32", workspace=ws)
     for a_, b_ in zip(first, (r3.out, r3.mask, r3.lse, r3.stats)):
         assert torch.equal(a_, b_)
+
+
+# ----------------------------------------------------------------------------- block-sparse prefill
+
+def _prefill_masked(inp, w, bm, lam, out="native"):
+    q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    if isinstance(bm, np.ndarray):
+        bm = torch.from_numpy(bm).cuda()
+    r = A.prefill_masked(q, k, v, bm, lam, causal=w.causal, br=w.br, bc=w.bc,
+                         out_dtype=OUT.get(out))
+    torch.cuda.synchronize()
+    return r
+
+
+def _check_masked_full(w, sel, lam, label, out="native"):
+    inp = synth.make_inputs(w)
+    res = _prefill_masked(inp, w, sel, lam, out)
+    tally = Tally()
+    nqt = synth.n_tiles(w.Nq, w.br)
+    for b in range(w.B):
+        for h in range(w.Hq):
+            for i in range(nqt):
+                prefill_masked_tile_parity(res, inp, w, lam, sel, b, h, i, tally)
+    m = res.mask.cpu().numpy()
+    assert (m[sel == 0] == 2).all(), "blocks outside the set must be reported not visited"
+    st = res.stats.cpu().numpy()
+    assert np.array_equal(st[..., 0], (m != 2).sum(axis=(2, 3)))
+    assert np.array_equal(st[..., 1], (m == 1).sum(axis=(2, 3)))
+    tally.check(w.dtype, label, out_bf16=res.out.dtype == torch.bfloat16)
+    return res
+
+
+MASKED_SHAPES = [
+    dict(B=1, Hq=2, Hkv=1, Nq=300, Nk=700, causal=True),
+    dict(B=2, Hq=2, Hkv=2, Nq=256, Nk=256, causal=True),
+    dict(B=1, Hq=2, Hkv=1, Nq=200, Nk=333, causal=False),
+]
+# (density, sink, local): CRISP-shaped sets, a set with rows that see nothing
+# (no sink, no local window), and the full set
+MASKED_SETS = [(0.3, True, 2), (0.2, False, 0), (1.0, True, 0)]
+
+
+@pytest.mark.parametrize("shape", MASKED_SHAPES)
+@pytest.mark.parametrize("bset", MASKED_SETS, ids=lambda x: f"d{x[0]}_sink{int(x[1])}_loc{x[2]}")
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-2, 6.0), (1.0, 6.0)])
+def test_prefill_masked_small(shape, bset, lam, gain):
+    w = synth.small_workload("prefill", d=128, dtype="bf16", br=128, bc=64, gain=gain, seed=41,
+                             window=32, **shape)
+    density, sink, local = bset
+    sel = synth.block_set(w, density, sink=sink, local=local, seed=1)
+    _check_masked_full(w, sel, lam, f"masked {shape} set={bset} lam={lam} g={gain}", "fp32")
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_prefill_masked_edge_sets(out):
+    """An empty set (every row zero, lse -inf, every block not visited), a set
+    holding only the tail tile past the last row's diagonal, and a set whose
+    only block is the ragged last key tile."""
+    w = synth.small_workload("prefill", B=1, Hq=2, Hkv=1, Nq=130, Nk=333, seed=43, gain=6.0)
+    inp = synth.make_inputs(w)
+    nqt, nkt = synth.n_tiles(w.Nq, w.br), synth.n_tiles(w.Nk, w.bc)
+    empty = np.zeros((1, 2, nqt, nkt), np.uint8)
+    r = _prefill_masked(inp, w, empty, 1e-2, out)
+    assert (r.out == 0).all() and (r.lse == -math.inf).all() and (r.mask == 2).all()
+    assert (r.stats == 0).all()
+    last = empty.copy()
+    last[..., nkt - 1] = 1  # causal: only the last query rows reach it
+    _check_masked_full(w, last, 1e-2, f"masked last-tile-only out={out}", out)
+    _check_masked_full(w.scaled(causal=False), last, 1e-2, f"masked tail non-causal out={out}", out)
+
+
+def test_prefill_masked_full_set_matches_prefill():
+    """With every block selected the block-sparse path is the plain kernel, bit for bit."""
+    w = synth.WORKLOADS[2].scaled(Nq=2048, Nk=3000, Hq=8, Hkv=2).with_gain(6.0)
+    inp = synth.make_inputs(w)
+    nqt, nkt = synth.n_tiles(w.Nq, w.br), synth.n_tiles(w.Nk, w.bc)
+    ones = torch.ones((1, 1, 1, nkt), dtype=torch.bool, device="cuda")  # broadcast set
+    for lam in (0.0, 1e-3, 1e-2):
+        ref = _prefill(inp, w, lam)
+        got = _prefill_masked(inp, w, ones, lam)
+        assert torch.equal(ref.out.view(torch.int16), got.out.view(torch.int16))
+        assert torch.equal(ref.lse, got.lse)
+        assert torch.equal(ref.mask, got.mask)
+        assert torch.equal(ref.stats, got.stats)
+
+
+def test_prefill_masked_broadcast_matches_expanded():
+    """A set shared over batch and heads (zero strides) equals the expanded copy."""
+    w = synth.small_workload("prefill", B=2, Hq=4, Hkv=2, Nq=400, Nk=900, seed=45, gain=6.0)
+    inp = synth.make_inputs(w)
+    sel = synth.block_set(w, 0.3, seed=2)[:1, :1]
+    shared = torch.from_numpy(sel).cuda()
+    a = _prefill_masked(inp, w, shared, 1e-2)
+    b = _prefill_masked(inp, w, shared.expand(2, 4, -1, -1).contiguous(), 1e-2)
+    assert torch.equal(a.out.view(torch.int16), b.out.view(torch.int16))
+    assert torch.equal(a.mask, b.mask) and torch.equal(a.stats, b.stats)
+
+
+@pytest.mark.parametrize("lam,gain,density", [(0.0, 1.0, 0.1), (1e-3, 6.0, 0.1), (1e-2, 6.0, 0.25)])
+def test_prefill_masked_llama8b_n32768(lam, gain, density):
+    """The benchmark's block-sparse configuration: sampled query tiles against
+    the oracle, whole-call invariants on the GPU mask."""
+    w = synth.WORKLOADS[2].with_gain(gain)
+    inp = synth.make_inputs(w)
+    sel = synth.block_set(w, density, seed=3)
+    res = _prefill_masked(inp, w, sel, lam, "bf16")
+    tally = Tally()
+    kv_cache = {}
+    for (h, i) in sample_qtiles(w, [0, 9, 31], 3, seed=4):
+        kvh = h // w.G
+        if kvh not in kv_cache:
+            kv_cache = {kvh: (synth.to_float(inp.k[0, kvh], w), synth.to_float(inp.v[0, kvh], w))}
+        kf, vf = kv_cache[kvh]
+        prefill_masked_tile_parity(res, inp, w, lam, sel, 0, h, i, tally, kf=kf, vf=vf)
+    m = res.mask.cpu().numpy()
+    nqt, nkt = m.shape[2], m.shape[3]
+    last_vis = (np.minimum((np.arange(nqt) + 1) * w.br, w.Nq) - 1 + w.Nk - w.Nq) // w.bc
+    reach = np.arange(nkt)[None, :] <= last_vis[:, None]
+    assert ((m != 2) == ((sel[0] != 0) & reach[None])).all()
+    assert (m[..., 0] == 1).all(), "the sink tile is selected and first: always kept"
+    st = res.stats.cpu().numpy()
+    assert np.array_equal(st[..., 1], (m == 1).sum(axis=(2, 3)))
+    tally.check(w.dtype, f"masked llama8b lam={lam} g={gain} density={density}", out_bf16=True)
 
 
 # ----------------------------------------------------------------------------- behaviour

@@ -549,12 +549,12 @@ MUTATIONS = {
     "running_max_not_updated": ("        m = m_new\n", "        m = np.maximum(m, 0 * m_new)\n"),
     "first_tile_not_forced": ("keep = (j == 0) or not (g < thr)", "keep = not (g < thr) and j >= 0"),
     "threshold_log10": ("math.log(lam)", "math.log10(lam)"),
-    "block_set_ignored": ("vis = visible(nq, nk, causal, r0, r1 - r0) & in_set[None, :]",
-                          "vis = visible(nq, nk, causal, r0, r1 - r0)"),
-    "block_set_wrong_query_tile": ("np.repeat(sel[b, hq, i], bc)[:nk]",
-                                   "np.repeat(sel[b, hq, 0], bc)[:nk]"),
-    "block_set_expanded_by_br": ("np.repeat(sel[b, hq, i], bc)[:nk]",
-                                 "np.repeat(sel[b, hq, i], br)[:nk]"),
+    "block_set_ignored": ("vis = visible(nq, nk, causal, row0, len(q_rows)) & in_set[None, :]",
+                          "vis = visible(nq, nk, causal, row0, len(q_rows))"),
+    "block_set_wrong_query_tile": ("v[b, kvh], sel[b, hq, i], lam,", "v[b, kvh], sel[b, hq, 0], lam,"),
+    "block_set_expanded_by_rows": ("np.repeat(np.asarray(sel_row) != 0, bc)[:nk]",
+                                   "np.repeat(np.asarray(sel_row) != 0, len(q_rows))[:nk]"),
+    "block_set_wrong_row_offset": ("causal, nq, r0, bc, scale)", "causal, nq, 0, bc, scale)"),
     "empty_rows_not_zeroed": ("np.where(seen[:, None], r.out, 0.0)", "r.out"),
 }
 

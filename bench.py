@@ -163,7 +163,7 @@ def bench_prefill(args):
                              unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
                              traffic=traffic, traffic_note=tnote,
                              algorithmic_flops_per_launch=alg,
-                             kernel="prefill_bf16_kernel", kernel_source_sha=sha))
+                             kernel="prefill_bf16_kernel<false>", kernel_source_sha=sha))
     sweep = []
     if not args.no_sweep:
         for gain in (1.0, 6.0):
@@ -176,7 +176,7 @@ def bench_prefill(args):
             base = None
             for lam in w.lambdas:
                 ms, _, r = time_calls(lambda: A.prefill(q2, k2, v2, lam, causal=True, br=w.br, bc=w.bc),
-                                      max(3, args.steps // 2), 1)
+                                      max(3, args.steps // 2), args.warmup)
                 base = ms if lam == 0.0 else base
                 sweep.append(dict(gain=gain, lam=lam, tflops=round(dense / (ms * 1e-3) / 1e12, 2),
                                   ms=round(ms, 4), skip_fraction=round(r.skip_fraction, 4),
@@ -207,9 +207,10 @@ def bench_prefill_masked(args, dense_ms):
         for density in (0.1, 0.25):
             bm = torch.from_numpy(synth.block_set(w, density, seed=3)).cuda()
             for lam in (0.0, args.lam):
+                # ~1 ms calls: warm up for tens of milliseconds so the clocks settle
                 ms, _, r = time_calls(lambda: A.prefill_masked(q, k, v, bm, lam, causal=True,
                                                                br=w.br, bc=w.bc),
-                                      max(3, args.steps // 2), 1)
+                                      max(3, args.steps // 2), max(args.warmup, 30))
                 alg, visited, kept = prefill_algorithmic_flops(w, r.stats)
                 tf = alg / (ms * 1e-3) / 1e12
                 rows.append(dict(gain=gain, density=density, lam=lam, ms=round(ms, 4),

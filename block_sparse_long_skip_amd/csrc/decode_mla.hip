@@ -18,34 +18,37 @@
 // running max before j, which for lambda <= 1 is the plain prefix max of the
 // tile maxima (a dropped tile never raises it). A split cannot know the maxima
 // of the splits before it, so the work runs in two passes plus a merge:
-//   pass 0 (speculative): every split runs the ordered tile loop with a running
-//     max that starts at -inf at its first tile, writes every tile max to the
-//     workspace, and leaves its partial (m, l, O) there;
-//   pass 1 (exact): every split takes the true prefix max at its first tile
-//     from the recorded tile maxima, derives the exact decision of every tile
-//     and head, writes the mask, the kept counts and the per-tile "some head
-//     keeps" flags, and compares with the decisions pass 0 took. Where they
-//     agree for every head of the group (always for the first split, and
-//     whenever nothing is dropped) the pass-0 partial is already exact. Where
-//     they differ the split is recomputed from the true prefix max, visiting
-//     only the tiles some head keeps, and its partial is replaced;
+//   pass 0 (speculative): every split runs the ordered tile loop; a split after
+//     the first scores tile 0 first (maxima only: it holds the attention sinks),
+//     so its running max starts from a lower bound of the exact one that
+//     usually equals it. It records every tile max and its own maximum in the
+//     workspace and leaves its partial (reference max, row sums, O) there;
+//   pass 1 (exact): every split takes the true running max entering it from the
+//     maxima of the earlier splits, derives the exact decision of every tile
+//     and head from the recorded tile maxima, and writes the mask, the kept
+//     counts and the per-tile "some head keeps" flags. The exact rule never
+//     keeps a tile the speculative one dropped (its running max is at least as
+//     large), so the pass-0 partial is exact unless some tile was kept only
+//     speculatively; only those tiles are read again, and their contribution
+//     at the partial's reference max is subtracted;
 //   merge: a log-sum-exp merge of the partials of each (batch, head).
 //
 // Workgroup layout (4 waves, 64 heads). Per key tile:
-//   * the 64 x 576 tile (72 KB) travels global -> LDS with
-//     global_load_lds_dwordx4 (no register staging), double-buffered, the next
-//     tile's copy issued at the top of the current one. The 16-byte chunk index
-//     is XOR-swizzled by the row so that both the score operand reads (16
-//     rows, one chunk) and the transposing value reads (4 rows, 2 chunks) hit
-//     distinct banks;
+//   * the 64 x 576 tile (72 KB) travels global -> LDS through buffer loads
+//     that write LDS directly (no register staging), double-buffered, the next
+//     tile's copy issued at the top of the current one. The tile is stored in
+//     1 KB blocks with the 16-byte chunk index XOR-swizzled by the row (see
+//     mla_off) so that both the score operand reads and the transposing value
+//     reads hit distinct banks;
 //   * wave w = (key half kh = w & 1, head half hh = w >> 1) computes
-//     S^T[32 keys][32 heads] = K q^T on v_mfma_f32_16x16x32_bf16, with its
+//     S^T[32 keys][32 heads] = K q^T on v_mfma_f32_32x32x16_bf16, with its
 //     heads' queries held in registers;
 //   * the per-head tile maxima of the two key halves meet in LDS; every wave
 //     then takes the same decision per head, and P^T (bf16) goes to LDS;
 //   * if any head keeps the tile, wave w computes output features
 //     128w..128w+127 of all 64 heads: O^T += V^T P^T, with V^T read from the
-//     key tile by ds_read_b64_tr_b16.
+//     key tile by ds_read_b64_tr_b16. The accumulators are rescaled lazily,
+//     only when a running max has grown by more than 2^8.
 #include <type_traits>
 #include <utility>
 

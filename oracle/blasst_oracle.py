@@ -282,6 +282,60 @@ def prefill_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_mask: np.n
     return OracleResult(out, lse, mask, gap, stats)
 
 
+def prefill_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
+                     mask: np.ndarray, causal: bool, br: int, bc: int,
+                     scale: Optional[float] = None) -> tuple:
+    """Gradients of a skip-softmax prefill with its tile mask held fixed.
+
+    Fine-tuning a model with the skip kernels in place improves its quality
+    (BLASST post, paragraph beginning "Все изменения можно делать без
+    дообучения"). The keep/drop decisions are a piecewise-constant function of
+    the inputs, so almost everywhere the gradient is that of softmax attention
+    over the kept tiles, the mask being a constant.
+
+    q [B,Hq,Nq,d], k [B,Hkv,Nk,d], v [B,Hkv,Nk,dv], dout [B,Hq,Nq,dv];
+    mask [B,Hq,nQt,nKt] as returned by the forward (1 = kept; 0 and 2 take no
+    part). Per query head, with A = causal visibility AND the expanded kept
+    tiles:
+        S = scale q k^T (-inf outside A);  P = row softmax of S over A (a row
+        with no allowed key has P = 0);  O = P v
+        dv = P^T dout;  dP = dout v^T;  delta = rowsum(dout * O)
+        dS = P * (dP - delta);  dq = scale dS k;  dk = scale dS^T q
+    and dk, dv of a KV head are the sums over the query heads that read it.
+    Returns (dq, dk, dv) in float64.
+    """
+    q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
+    B, Hq, nq, d = q.shape
+    hkv, nk = k.shape[1], k.shape[2]
+    if Hq % hkv:
+        raise ValueError("Hq must be a multiple of Hkv")
+    if scale is None:
+        scale = default_scale(d)
+    G = Hq // hkv
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    vis = visible(nq, nk, causal)
+    for b in range(B):
+        for hq in range(Hq):
+            kvh = hq // G
+            allowed = vis & expand_tile_mask(mask[b, hq], br, bc, nq, nk)
+            s = np.where(allowed, scale * (q[b, hq] @ k[b, kvh].T), -np.inf)
+            mx = s.max(axis=1, keepdims=True)
+            live = np.isfinite(mx)
+            e = np.exp(s - np.where(live, mx, 0.0))
+            den = e.sum(axis=1, keepdims=True)
+            p = np.where(live, e / np.where(live, den, 1.0), 0.0)
+            o = p @ v[b, kvh]
+            dv[b, kvh] += p.T @ dout[b, hq]
+            dp = dout[b, hq] @ v[b, kvh].T
+            delta = (dout[b, hq] * o).sum(axis=1, keepdims=True)
+            ds = p * (dp - delta)
+            dq[b, hq] = scale * (ds @ k[b, kvh])
+            dk[b, kvh] += scale * (ds.T @ q[b, hq])
+    return dq, dk, dv
+
+
 def decode_row(q: np.ndarray, k: np.ndarray, v: np.ndarray, b: int, hq: int,
                lam: float, bc: int, scale: Optional[float] = None) -> TileRowResult:
     """One (batch b, query head hq) decode row: a single query that sees every key.
@@ -371,7 +425,7 @@ def masked_dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np
 
 __all__ = [
     "threshold", "default_scale", "visible", "blasst_rows", "prefill_tile", "prefill",
-    "block_sparse_rows", "prefill_masked",
+    "block_sparse_rows", "prefill_masked", "prefill_backward",
     "decode_row", "decode", "naive_attention", "expand_tile_mask", "masked_dense_attention",
     "OracleResult", "TileRowResult", "MASK_SKIPPED", "MASK_KEPT", "MASK_NOT_VISITED",
 ]

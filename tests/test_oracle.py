@@ -442,10 +442,101 @@ def pin_block_sparse_brute(orc):
         assert r.stats[0, 0].tolist() == [int((r.mask[0, 0] != 2).sum()), int((r.mask[0, 0] == 1).sum())]
 
 
+def _allowed(mask_row, causal, br, bc, Nq, Nk):
+    """[Nq, Nk] booleans from a tile mask row (1 = kept) and causality, from scratch."""
+    r = np.arange(Nq)[:, None]
+    c = np.arange(Nk)[None, :]
+    ok = (np.asarray(mask_row) == 1)[r // br, c // bc]
+    if causal:
+        ok = ok & (c <= r + Nk - Nq)
+    return ok
+
+
+def _bwd_case(rng, orc, B, Hq, Hkv, Nq, Nk, d, br, bc, causal, lam, empty_rows=False):
+    q, k, v = _rand_case(rng, B, Hq, Hkv, Nq, Nk, d, d, plant=5.0)
+    dout = rng.standard_normal((B, Hq, Nq, d))
+    mask = orc.prefill(q, k, v, lam, causal, br, bc).mask.copy()
+    if empty_rows:  # a block-sparse forward whose first query tile saw nothing
+        mask[:, :, 0, :] = np.where(mask[:, :, 0, :] == 2, 2, 0)
+    return q, k, v, dout, mask
+
+
+def pin_backward_autograd(orc):
+    """Gradients equal torch autograd (CPU, float64) of softmax attention over the
+    allowed elements, the loss being sum(dout * out)."""
+    rng = np.random.default_rng(16)
+    n_dropped = 0
+    for (B, Hq, Hkv, Nq, Nk, d, br, bc, causal, lam, empty) in [
+        (1, 4, 2, 40, 70, 8, 8, 8, True, 1e-2, False),
+        (2, 2, 1, 33, 50, 4, 5, 7, False, 1e-1, False),
+        (1, 2, 2, 24, 24, 4, 8, 4, True, 0.0, True),
+    ]:
+        q, k, v, dout, mask = _bwd_case(rng, orc, B, Hq, Hkv, Nq, Nk, d, br, bc, causal, lam, empty)
+        n_dropped += int((mask == 0).sum())
+        sc = 1.0 / math.sqrt(d)
+        dq, dk, dv = orc.prefill_backward(q, k, v, dout, mask, causal, br, bc)
+        tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+        loss = torch.zeros((), dtype=torch.float64)
+        G = Hq // Hkv
+        for b in range(B):
+            for h in range(Hq):
+                ok = _allowed(mask[b, h], causal, br, bc, Nq, Nk)
+                rows = ok.any(axis=1)
+                okt = torch.from_numpy(ok[rows])
+                s_ = sc * tq[b, h][torch.from_numpy(rows)] @ tk[b, h // G].T
+                p_ = torch.softmax(s_.masked_fill(~okt, -math.inf), dim=-1)
+                o_ = p_ @ tv[b, h // G]
+                loss = loss + (o_ * torch.from_numpy(dout[b, h][rows])).sum()
+        loss.backward()
+        for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+            assert np.abs(got - ref.numpy()).max() < 1e-12
+        if empty:
+            assert (dq[:, :, :br] == 0).all()
+    assert n_dropped > 0, "fixture must exercise dropped tiles"
+
+
+def pin_backward_finite_difference(orc):
+    """Central differences of sum(dout * out) with the mask held fixed; the
+    forward here is a plain loop over the allowed keys."""
+    rng = np.random.default_rng(17)
+    B, Hq, Hkv, Nq, Nk, d, br, bc = 1, 2, 1, 5, 7, 3, 2, 3
+    q, k, v, dout, mask = _bwd_case(rng, orc, B, Hq, Hkv, Nq, Nk, d, br, bc, True, 0.3)
+    sc = 1.0 / math.sqrt(d)
+
+    def loss(q_, k_, v_):
+        total = 0.0
+        for h in range(Hq):
+            ok = _allowed(mask[0, h], True, br, bc, Nq, Nk)
+            for r in range(Nq):
+                cs = [c for c in range(Nk) if ok[r, c]]
+                if not cs:
+                    continue
+                sco = [sc * float(q_[0, h, r] @ k_[0, 0, c]) for c in cs]
+                mx = max(sco)
+                w = [math.exp(x - mx) for x in sco]
+                for x in range(d):
+                    o = sum(wi * v_[0, 0, c, x] for wi, c in zip(w, cs)) / sum(w)
+                    total += dout[0, h, r, x] * o
+        return total
+
+    dq, dk, dv = orc.prefill_backward(q, k, v, dout, mask, True, br, bc)
+    hstep = 1e-6
+    for arr, grad in ((q, dq), (k, dk), (v, dv)):
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + hstep
+            lp = loss(q, k, v)
+            arr[idx] = keep - hstep
+            lm = loss(q, k, v)
+            arr[idx] = keep
+            assert abs((lp - lm) / (2 * hstep) - grad[idx]) < 1e-6, idx
+
+
 PINS = [pin_hand_example, pin_row_aggregation, pin_tie, pin_causal_visibility,
         pin_lambda0_sdpa, pin_bottom_right_causal, pin_masked_sdpa, pin_closed_form_mask,
         pin_brute_force, pin_decode_sdpa, pin_block_sparse_sdpa, pin_block_sparse_kept,
-        pin_block_sparse_full_set, pin_block_sparse_brute]
+        pin_block_sparse_full_set, pin_block_sparse_brute, pin_backward_autograd,
+        pin_backward_finite_difference]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -556,6 +647,14 @@ MUTATIONS = {
                                    "np.repeat(np.asarray(sel_row) != 0, len(q_rows))[:nk]"),
     "block_set_wrong_row_offset": ("causal, nq, r0, bc, scale)", "causal, nq, 0, bc, scale)"),
     "empty_rows_not_zeroed": ("np.where(seen[:, None], r.out, 0.0)", "r.out"),
+    "bwd_dq_missing_scale": ("dq[b, hq] = scale * (ds @ k[b, kvh])", "dq[b, hq] = (ds @ k[b, kvh])"),
+    "bwd_delta_dropped": ("ds = p * (dp - delta)", "ds = p * dp"),
+    "bwd_dk_not_summed_over_group": ("dk[b, kvh] += scale * (ds.T @ q[b, hq])",
+                                     "dk[b, kvh] = scale * (ds.T @ q[b, hq])"),
+    "bwd_mask_ignored": ("allowed = vis & expand_tile_mask(mask[b, hq], br, bc, nq, nk)", "allowed = vis"),
+    "bwd_unnormalised_p": ("p = np.where(live, e / np.where(live, den, 1.0), 0.0)",
+                           "p = np.where(live, e, 0.0)"),
+    "bwd_dk_uses_dp": ("dk[b, kvh] += scale * (ds.T @ q[b, hq])", "dk[b, kvh] += scale * (dp.T @ q[b, hq])"),
 }
 
 

@@ -29,7 +29,8 @@ STATUS = {
 }
 
 # Every symbol include/blasst.h declares.
-EXPORTED = ("blasst_attn_prefill", "blasst_attn_prefill_masked", "blasst_attn_decode",
+EXPORTED = ("blasst_attn_prefill", "blasst_attn_prefill_masked", "blasst_attn_prefill_backward",
+            "blasst_prefill_backward_workspace_size", "blasst_attn_decode",
             "blasst_decode_workspace_size", "blasst_status_string", "blasst_last_error",
             "blasst_version")
 
@@ -77,6 +78,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                ctypes.c_int, ctypes.c_int, ctypes.c_float,
                                                ctypes.c_float, ctypes.c_int, ctypes.c_int,
                                                ctypes.c_int, vp]
+    lib.blasst_attn_prefill_backward.restype = ctypes.c_int
+    lib.blasst_attn_prefill_backward.argtypes = [vp, vp, vp, vp, vp, fp, u8p, fp, fp, fp,
+                                                 ctypes.POINTER(Shape), ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_float, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int, vp, ctypes.c_size_t,
+                                                 vp]
+    lib.blasst_prefill_backward_workspace_size.restype = ctypes.c_int
+    lib.blasst_prefill_backward_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int,
+                                                           ctypes.c_int, ctypes.c_int,
+                                                           ctypes.c_int,
+                                                           ctypes.POINTER(ctypes.c_size_t)]
     lib.blasst_attn_decode.restype = ctypes.c_int
     lib.blasst_attn_decode.argtypes = [vp, vp, vp, vp, u8p, fp, i64p, ctypes.POINTER(Shape),
                                        ctypes.c_int, ctypes.c_int, ctypes.c_float,
@@ -213,6 +225,45 @@ def prefill_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, block_mask
     return AttnResult(out, mask, lse, stats)
 
 
+def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: torch.Tensor,
+                     dout: torch.Tensor, lse: torch.Tensor, mask: torch.Tensor,
+                     causal: bool = True, br: int = 128, bc: int = 64,
+                     scale: Optional[float] = None,
+                     workspace: Optional[torch.Tensor] = None) -> tuple:
+    """Gradients (dq, dk, dv), float32, of a bf16 skip-softmax prefill with its
+    tile mask held fixed. out, lse and mask are the forward's outputs; dout is
+    the gradient of the loss with respect to out (bf16)."""
+    lib = load_library()
+    _require_device(q, k, v, out, dout, lse, mask)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk, dv_ = k.shape[1], k.shape[2], v.shape[3]
+    dev = q.device
+    if dout.dtype != torch.bfloat16:
+        raise TypeError("dout must be bfloat16")
+    if dout.stride() != out.stride():
+        dout, out = dout.contiguous(), out.contiguous()
+    lse = lse.contiguous()
+    mask = mask.contiguous()
+    dq = torch.empty_strided(q.shape, q.stride(), dtype=torch.float32, device=dev)
+    dk = torch.empty_strided(k.shape, k.stride(), dtype=torch.float32, device=dev)
+    dv = torch.empty_strided(v.shape, v.stride(), dtype=torch.float32, device=dev)
+    sh = Shape(B, Hq, Hkv, Nq, Nk, d, dv_, _strides3(q), _strides3(k), _strides3(v),
+               _strides3(out))
+    n = ctypes.c_size_t(0)
+    _check(lib.blasst_prefill_backward_workspace_size(ctypes.byref(sh), _dtype_code(q.dtype),
+                                                      int(bool(causal)), int(br), int(bc),
+                                                      ctypes.byref(n)))
+    if workspace is None:
+        workspace = _workspace(n.value, dev)
+    st = lib.blasst_attn_prefill_backward(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(dout), _ptr(lse), _ptr(mask), _ptr(dq),
+        _ptr(dk), _ptr(dv), ctypes.byref(sh), _dtype_code(q.dtype), _dtype_code(out.dtype),
+        float(scale) if scale else 0.0, int(bool(causal)), int(br), int(bc), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st)
+    return dq, dk, dv
+
+
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], lam: float,
            bc: int = 64, scale: Optional[float] = None, dv: Optional[int] = None,
            out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
@@ -282,5 +333,5 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
-__all__ = ["prefill", "prefill_masked", "decode", "decode_workspace_size", "load_library", "Shape", "BlasstError", "AttnResult",
+__all__ = ["prefill", "prefill_masked", "prefill_backward", "decode", "decode_workspace_size", "load_library", "Shape", "BlasstError", "AttnResult",
            "EXPORTED", "LIB_PATH", "STATUS"]

@@ -18,6 +18,7 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeArgs& a, void* workspace, hipStream_t stream);
+hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream);
 size_t decode_mla_workspace_bytes(int B, int Hq, int Hkv, int G, int nkt);
 
 __global__ void zero_i64_kernel(int64_t* p, int64_t n) {
@@ -335,6 +336,118 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
   const hipError_t e = kind == DecodeKernel::kGqa ? blasst::launch_decode_gqa(a, hs)
                                                   : blasst::launch_decode_mla(a, workspace, hs);
   return hip_status(e, "decode launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the backward entry point and its workspace query.
+blasst_status_t check_backward(const blasst_shape_t& s, blasst_dtype_t dtype, int causal, int br,
+                               int bc) {
+  if (s.batch < 0 || s.heads_q < 1 || s.heads_kv < 1 || s.len_q < 0 || s.len_kv < 1 ||
+      s.d_qk < 1 || s.d_v < 1)
+    return fail(BLASST_E_SHAPE, "sizes out of range (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d dv=%d)",
+                s.batch, s.heads_q, s.heads_kv, s.len_q, s.len_kv, s.d_qk, s.d_v);
+  if (s.heads_q % s.heads_kv != 0)
+    return fail(BLASST_E_SHAPE, "heads_q (%d) must be a multiple of heads_kv (%d)", s.heads_q,
+                s.heads_kv);
+  if (causal && s.len_q > s.len_kv)
+    return fail(BLASST_E_SHAPE, "causal prefill needs len_q <= len_kv (%d > %d)", s.len_q,
+                s.len_kv);
+  if (br < 1 || bc < 1) return fail(BLASST_E_SHAPE, "tile sizes must be positive");
+  if (dtype != BLASST_FP32 && dtype != BLASST_BF16)
+    return fail(BLASST_E_DTYPE, "unknown dtype %d", (int)dtype);
+  if (dtype != BLASST_BF16 || s.d_qk != 128 || s.d_v != 128 || br != 128 || bc != 64)
+    return fail(BLASST_E_UNSUPPORTED,
+                "no backward kernel for dtype=%d d_qk=%d d_v=%d br=%d bc=%d (supported: bf16 "
+                "128/128 128x64)",
+                (int)dtype, s.d_qk, s.d_v, br, bc);
+  const int64_t nqt = ((int64_t)s.len_q + br - 1) / br;
+  const int64_t nkt = ((int64_t)s.len_kv + bc - 1) / bc;
+  if (nqt > blasst::kBackwardMaxTiles || nkt > blasst::kBackwardMaxTiles)
+    return fail(BLASST_E_UNSUPPORTED, "backward supports at most %d query and key tiles",
+                blasst::kBackwardMaxTiles);
+  if ((int64_t)s.batch * s.heads_q * nqt > 0x7fffffffLL ||
+      (int64_t)s.batch * s.heads_kv * nkt > 0x7fffffffLL)
+    return fail(BLASST_E_UNSUPPORTED, "grid too large");
+  if (s.k_stride[2] < s.d_qk || s.v_stride[2] < s.d_v || s.q_stride[2] < s.d_qk ||
+      s.o_stride[2] < s.d_v)
+    return fail(BLASST_E_SHAPE, "rows overlap (position stride below the row length)");
+  if (s.k_stride[2] > (1 << 24) || s.v_stride[2] > (1 << 24) || s.q_stride[2] > (1 << 24) ||
+      s.o_stride[2] > (1 << 24))
+    return fail(BLASST_E_UNSUPPORTED, "backward needs position strides <= 2^24 elements");
+  return BLASST_OK;
+}
+
+size_t backward_workspace(const blasst_shape_t& s) {
+  const size_t n = (size_t)s.batch * s.heads_q * s.len_q * sizeof(float);
+  return (n + 255) & ~(size_t)255;
+}
+
+}  // namespace
+
+extern "C" {
+
+blasst_status_t blasst_prefill_backward_workspace_size(const blasst_shape_t* shape,
+                                                       blasst_dtype_t dtype, int causal, int br,
+                                                       int bc, size_t* bytes) {
+  if (!shape || !bytes) return fail(BLASST_E_NULL, "shape and bytes are required");
+  const blasst_status_t st = check_backward(*shape, dtype, causal, br, bc);
+  if (st != BLASST_OK) return st;
+  *bytes = backward_workspace(*shape);
+  return ok();
+}
+
+blasst_status_t blasst_attn_prefill_backward(
+    const void* q, const void* k, const void* v, const void* out, const void* dout,
+    const float* lse, const uint8_t* mask, float* dq, float* dk, float* dv,
+    const blasst_shape_t* shape, blasst_dtype_t dtype, blasst_dtype_t out_dtype, float scale,
+    int causal, int br, int bc, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
+  if (!q || !k || !v || !out || !dout || !lse || !mask || !dq || !dk || !dv)
+    return fail(BLASST_E_NULL, "q, k, v, out, dout, lse, mask, dq, dk and dv are required");
+  const blasst_shape_t& s = *shape;
+  blasst_status_t st = check_backward(s, dtype, causal, br, bc);
+  if (st != BLASST_OK) return st;
+  if (out_dtype != BLASST_FP32 && out_dtype != BLASST_BF16)
+    return fail(BLASST_E_DTYPE, "unknown out_dtype %d", (int)out_dtype);
+  if (!std::isfinite(scale)) return fail(BLASST_E_ARG, "scale must be finite");
+  const int oelem = out_dtype == BLASST_FP32 ? 4 : 2;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) || !aligned16(dout) ||
+      !aligned16(dq) || !aligned16(dk) || !aligned16(dv))
+    return fail(BLASST_E_ALIGN, "q, k, v, out, dout, dq, dk and dv must be 16-byte aligned");
+  if (!strides_aligned(s.q_stride, 3, 2) || !strides_aligned(s.k_stride, 3, 2) ||
+      !strides_aligned(s.v_stride, 3, 2) || !strides_aligned(s.o_stride, 3, 2) ||
+      !strides_aligned(s.o_stride, 3, oelem))
+    return fail(BLASST_E_ALIGN, "every stride times the element size must be a multiple of 16");
+  const size_t need = backward_workspace(s);
+  if (need > 0) {
+    if (!workspace) return fail(BLASST_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (workspace_bytes < need)
+      return fail(BLASST_E_WORKSPACE, "workspace of %zu bytes is smaller than %zu", workspace_bytes,
+                  need);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(BLASST_E_WORKSPACE, "workspace must be 256-byte aligned");
+  }
+  const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)s.d_qk));
+  blasst::BackwardArgs a;
+  a.q = q; a.k = k; a.v = v; a.out = out; a.dout = dout; a.lse = lse; a.mask = mask;
+  a.dq = dq; a.dk = dk; a.dv = dv; a.delta = static_cast<float*>(workspace);
+  a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nq = s.len_q; a.Nk = s.len_kv;
+  a.nqt = (s.len_q + br - 1) / br; a.nkt = (s.len_kv + bc - 1) / bc;
+  a.causal = causal ? 1 : 0;
+  a.out_f32 = out_dtype == BLASST_FP32 ? 1 : 0;
+  a.qs0 = s.q_stride[0]; a.qs1 = s.q_stride[1]; a.qs2 = s.q_stride[2];
+  a.ks0 = s.k_stride[0]; a.ks1 = s.k_stride[1]; a.ks2 = s.k_stride[2];
+  a.vs0 = s.v_stride[0]; a.vs1 = s.v_stride[1]; a.vs2 = s.v_stride[2];
+  a.os0 = s.o_stride[0]; a.os1 = s.o_stride[1]; a.os2 = s.o_stride[2];
+  a.dos0 = s.o_stride[0]; a.dos1 = s.o_stride[1]; a.dos2 = s.o_stride[2];
+  a.scale = sc;
+  a.scale_log2 = sc * blasst::kLog2e;
+  if (s.batch == 0) return ok();
+  return hip_status(blasst::launch_backward_bf16(a, reinterpret_cast<hipStream_t>(stream)),
+                    "backward launch");
 }
 
 }  // extern "C"

@@ -43,6 +43,33 @@ struct PrefillArgs {
   float thr_raw;    // ln(lambda) / scale: the drop threshold in raw q.k units
 };
 
+// Longest list of kept tiles (key tiles of a query tile, or query tiles of a
+// key tile) the backward kernels hold in LDS.
+constexpr int kBackwardMaxTiles = 6144;
+
+// Arguments of the backward kernels (element strides; last dim contiguous).
+// The gradients dq, dk, dv are float32 with the element strides of q, k, v;
+// dout has the strides of out.
+struct BackwardArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* out;    // forward output, bf16 or float32 (out_f32)
+  const void* dout;   // bf16
+  const float* lse;   // [B,Hq,Nq] forward lse
+  const uint8_t* mask;  // [B,Hq,nqt,nkt] forward mask, 1 = kept
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;       // workspace [B,Hq,Nq]
+  int B, Hq, Hkv, Nq, Nk;
+  int nqt, nkt;
+  int causal;
+  int out_f32;
+  int64_t qs0, qs1, qs2, ks0, ks1, ks2, vs0, vs1, vs2, os0, os1, os2, dos0, dos1, dos2;
+  float scale, scale_log2;
+};
+
 // Arguments of the decode kernels.
 struct DecodeArgs {
   const void* q;

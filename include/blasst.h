@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define BLASST_VERSION 210 /* 2.1.0: block-sparse prefill */
+#define BLASST_VERSION 220 /* 2.2.0: prefill backward */
 
 typedef enum blasst_status {
   BLASST_OK = 0,
@@ -70,8 +70,8 @@ typedef enum blasst_status {
   BLASST_E_UNSUPPORTED = 6, /* valid request with no kernel in this build */
   BLASST_E_ARG = 7,         /* other bad scalar argument (non-finite scale) */
   BLASST_E_HIP = 8,         /* a HIP runtime call failed */
-  BLASST_E_WORKSPACE = 9    /* decode workspace NULL, smaller than
-                               blasst_decode_workspace_size() or not 256-byte
+  BLASST_E_WORKSPACE = 9    /* workspace NULL, smaller than the size its
+                               query function returns, or not 256-byte
                                aligned */
 } blasst_status_t;
 
@@ -170,6 +170,52 @@ blasst_status_t blasst_attn_prefill_masked(const void* q, const void* k, const v
                                            blasst_dtype_t dtype, blasst_dtype_t out_dtype,
                                            float lambda, float scale, int causal, int br, int bc,
                                            void* stream);
+
+/*
+ * Prefill backward: gradients of a bf16 skip-softmax prefill with its tile
+ * mask held fixed. Fine-tuning a model with the skip kernels in place improves
+ * its quality (the BLASST post, paragraph beginning "Все изменения можно
+ * делать без дообучения"); the keep/drop decisions are piecewise constant in
+ * the inputs, so the gradient is that of softmax attention over the kept
+ * tiles. With A = causal visibility AND the kept tiles of `mask`, and
+ * P = exp(scale q.k - lse) on A (0 elsewhere):
+ *   dv = P^T dout,  dP = dout v^T,  delta = rowsum(dout * out),
+ *   dS = P (dP - delta),  dq = scale dS k,  dk = scale dS^T q,
+ * dk and dv of a KV head summed over the query heads that read it.
+ *
+ *   q, k, v    the forward's inputs (bf16), strides as in the shape
+ *   out        the forward's output, element type out_dtype, strides o_stride
+ *   dout       gradient of the loss with respect to out, bf16, strides o_stride
+ *   lse        the forward's lse_out, contiguous float [B, Hq, Nq] (a row with
+ *              lse = -inf, one that saw no key, gets no gradient)
+ *   mask       the forward's mask_out, contiguous uint8 [B, Hq, ceil(Nq/br),
+ *              ceil(Nk/bc)]; only tiles marked BLASST_TILE_KEPT take part
+ *   dq, dk, dv float outputs with the element strides of q, k and v; every
+ *              element is written (rows of keys no query keeps get zeros)
+ *   workspace  device memory of at least blasst_prefill_backward_workspace_size()
+ *              bytes (B * Hq * Nq floats), 256-byte aligned, owned by the
+ *              caller; contents on entry are ignored. Calls that overlap in
+ *              time must not share it.
+ *
+ * Supported (else BLASST_E_UNSUPPORTED): BLASST_BF16, d_qk = d_v = 128,
+ * br = 128, bc = 64, at most 6144 query tiles and 6144 key tiles, position
+ * strides at most 2^24 elements. Any mask produced by blasst_attn_prefill or
+ * blasst_attn_prefill_masked with these tiles is accepted.
+ */
+blasst_status_t blasst_attn_prefill_backward(
+    const void* q, const void* k, const void* v, const void* out, const void* dout,
+    const float* lse, const uint8_t* mask, float* dq, float* dk, float* dv,
+    const blasst_shape_t* shape, blasst_dtype_t dtype, blasst_dtype_t out_dtype, float scale,
+    int causal, int br, int bc, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Workspace bytes blasst_attn_prefill_backward needs for this shape. Validates
+ * like the call (sizes, dtype, supported combination) and writes *bytes only
+ * on BLASST_OK. Launches nothing.
+ */
+blasst_status_t blasst_prefill_backward_workspace_size(const blasst_shape_t* shape,
+                                                       blasst_dtype_t dtype, int causal, int br,
+                                                       int bc, size_t* bytes);
 
 /*
  * Decode: one query token per (batch, query head) against a contiguous KV

@@ -284,7 +284,8 @@ def prefill_masked(q: np.ndarray, k: np.ndarray, v: np.ndarray, block_mask: np.n
 
 def prefill_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarray,
                      mask: np.ndarray, causal: bool, br: int, bc: int,
-                     scale: Optional[float] = None) -> tuple:
+                     scale: Optional[float] = None, magnitudes: bool = False,
+                     out: Optional[np.ndarray] = None) -> tuple:
     """Gradients of a skip-softmax prefill with its tile mask held fixed.
 
     Fine-tuning a model with the skip kernels in place improves its quality
@@ -302,7 +303,12 @@ def prefill_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarr
         dv = P^T dout;  dP = dout v^T;  delta = rowsum(dout * O)
         dS = P * (dP - delta);  dq = scale dS k;  dk = scale dS^T q
     and dk, dv of a KV head are the sums over the query heads that read it.
-    Returns (dq, dk, dv) in float64.
+    out, if given, is the stored forward output [B,Hq,Nq,dv] that delta is taken
+    from (an implementation saves the output in the type it was written in);
+    by default delta uses the exact output P v.
+    Returns (dq, dk, dv) in float64; with magnitudes=True also the sums of the
+    absolute values of the products each element is made of (scale |dS| |k|,
+    scale |dS|^T |q|, |P|^T |dout|), the scale of a rounding-error bound.
     """
     q, k, v, dout = (np.asarray(x, dtype=np.float64) for x in (q, k, v, dout))
     B, Hq, nq, d = q.shape
@@ -315,6 +321,7 @@ def prefill_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarr
     dq = np.zeros_like(q)
     dk = np.zeros_like(k)
     dv = np.zeros_like(v)
+    mq, mk, mv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
     vis = visible(nq, nk, causal)
     for b in range(B):
         for hq in range(Hq):
@@ -329,10 +336,18 @@ def prefill_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, dout: np.ndarr
             o = p @ v[b, kvh]
             dv[b, kvh] += p.T @ dout[b, hq]
             dp = dout[b, hq] @ v[b, kvh].T
+            if out is not None:
+                o = np.asarray(out[b, hq], dtype=np.float64)
             delta = (dout[b, hq] * o).sum(axis=1, keepdims=True)
             ds = p * (dp - delta)
             dq[b, hq] = scale * (ds @ k[b, kvh])
             dk[b, kvh] += scale * (ds.T @ q[b, hq])
+            if magnitudes:
+                mq[b, hq] = scale * (np.abs(ds) @ np.abs(k[b, kvh]))
+                mk[b, kvh] += scale * (np.abs(ds).T @ np.abs(q[b, hq]))
+                mv[b, kvh] += p.T @ np.abs(dout[b, hq])
+    if magnitudes:
+        return dq, dk, dv, mq, mk, mv
     return dq, dk, dv
 
 

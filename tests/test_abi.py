@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(A.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.blasst_version() == 210
+    assert lib.blasst_version() == 220
 
 
 def test_status_strings():
@@ -167,6 +167,69 @@ def test_prefill_masked_validation(case, expect):
         kw["lam"] = -1.0
     assert _prefill_masked(sh, **kw) == expect, _err()
     assert _err() != ""
+
+
+def _backward(sh, dtype=BF16, br=128, bc=64, ws=P, ws_bytes=1 << 30, q=P, lse=P, scale=0.0,
+              out_dtype=None, causal=1):
+    lib = A.load_library()
+    return lib.blasst_attn_prefill_backward(q, P, P, P, P, lse, P, P, P, P, ctypes.byref(sh), dtype,
+                                            dtype if out_dtype is None else out_dtype, scale,
+                                            causal, br, bc, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_q", 1), ("null_lse", 1), ("f32", 6), ("bad_d", 6), ("bad_tile", 6), ("heads", 2),
+    ("causal_nq_gt_nk", 2), ("no_workspace", 9), ("small_workspace", 9),
+    ("misaligned_workspace", 9), ("scale_inf", 7), ("misaligned_stride", 5),
+    ("overlapping_rows", 2), ("too_many_tiles", 6), ("bad_out_dtype", 3),
+])
+def test_prefill_backward_validation(case, expect):
+    sh = _shape()
+    kw = {}
+    if case == "null_q":
+        kw["q"] = None
+    elif case == "null_lse":
+        kw["lse"] = None
+    elif case == "f32":
+        sh = _shape(d=64, dv=64)
+        kw["dtype"], kw["br"] = FP32, 64
+    elif case == "bad_d":
+        sh.d_qk = sh.d_v = 96
+    elif case == "bad_tile":
+        kw["bc"] = 128
+    elif case == "heads":
+        sh.heads_q = 3
+    elif case == "causal_nq_gt_nk":
+        sh.len_q, sh.len_kv = 300, 200
+    elif case == "no_workspace":
+        kw["ws"] = None
+    elif case == "small_workspace":
+        kw["ws_bytes"] = 16
+    elif case == "misaligned_workspace":
+        kw["ws"] = P + 16
+    elif case == "scale_inf":
+        kw["scale"] = math.inf
+    elif case == "misaligned_stride":
+        sh.q_stride[1] += 4  # 8 bytes, not a multiple of 16
+    elif case == "overlapping_rows":
+        sh.k_stride[2] = 64
+    elif case == "too_many_tiles":
+        sh = _shape(Nq=128, Nk=6144 * 64 + 1)
+    elif case == "bad_out_dtype":
+        kw["out_dtype"] = 7
+    assert _backward(sh, **kw) == expect, _err()
+    assert _err() != ""
+
+
+def test_prefill_backward_workspace_size():
+    lib = A.load_library()
+    n = ctypes.c_size_t(7)
+    sh = _shape(B=2, Hq=4, Hkv=2, Nq=300, Nk=700)
+    assert lib.blasst_prefill_backward_workspace_size(ctypes.byref(sh), BF16, 1, 128, 64,
+                                                      ctypes.byref(n)) == 0, _err()
+    assert n.value >= 2 * 4 * 300 * 4 and n.value % 256 == 0
+    assert lib.blasst_prefill_backward_workspace_size(ctypes.byref(sh), FP32, 1, 128, 64,
+                                                      ctypes.byref(n)) == 6
 
 
 @pytest.mark.parametrize("case,expect", [

@@ -685,3 +685,35 @@ def test_pins_catch_planted_mistake(name):
         assert caught == []
     else:
         assert caught, f"no pin caught mutation {name}"
+
+
+def test_backward_magnitudes_bound_the_gradients():
+    """The error-scale tensors the backward parity bar uses are sums of absolute
+    products, so they bound the gradients themselves (triangle inequality)."""
+    rng = np.random.default_rng(18)
+    q, k, v, dout, mask = _bwd_case(rng, oracle, 1, 4, 2, 40, 70, 8, 8, 8, True, 1e-2)
+    dq, dk, dv, mq, mk, mv = oracle.prefill_backward(q, k, v, dout, mask, True, 8, 8, magnitudes=True)
+    plain = oracle.prefill_backward(q, k, v, dout, mask, True, 8, 8)
+    for g, m, p in ((dq, mq, plain[0]), (dk, mk, plain[1]), (dv, mv, plain[2])):
+        assert np.array_equal(g, p)
+        assert (np.abs(g) <= m * (1 + 1e-12) + 1e-300).all()
+        assert (m > 0).any()
+
+
+def test_backward_stored_output_only_changes_delta():
+    """Passing the exact output as the stored one changes nothing; a perturbed
+    stored output moves dq and dk (through delta) but not dv."""
+    rng = np.random.default_rng(19)
+    q, k, v, dout, mask = _bwd_case(rng, oracle, 1, 2, 1, 24, 40, 4, 8, 8, True, 1e-2)
+    ref = oracle.prefill_backward(q, k, v, dout, mask, True, 8, 8)
+    o = oracle.masked_dense_attention  # exact output per head
+    out = np.zeros(dout.shape)
+    for h in range(2):
+        keep = _allowed(mask[0, h], True, 8, 8, 24, 40)
+        out[0, h] = o(q[0, h], k[0, 0], v[0, 0], keep, False)[0]
+    same = oracle.prefill_backward(q, k, v, dout, mask, True, 8, 8, out=out)
+    for a_, b_ in zip(ref, same):
+        assert np.abs(a_ - b_).max() < 1e-12
+    moved = oracle.prefill_backward(q, k, v, dout, mask, True, 8, 8, out=out * 1.01)
+    assert np.abs(moved[0] - ref[0]).max() > 1e-6 and np.abs(moved[1] - ref[1]).max() > 1e-6
+    assert np.abs(moved[2] - ref[2]).max() == 0

@@ -27,6 +27,9 @@ inputs already resident in HBM. The line printed on stdout carries:
                block-sparse prefill methods (sink tile, local window, vertical
                columns, scattered blocks) at densities 0.1 and 0.25: algorithmic
                TFLOP/s of the selected work and speed-up over dense lambda = 0
+  prefill_backward
+               dq, dk, dv of the same layer with the forward's mask held fixed:
+               algorithmic TFLOP/s (5 products per kept tile) against the peak
   decode       the batch-32 GQA decode over 65536 keys and the batch-16 MLA
                decode over 32768 latent keys: GB/s of the bytes actually read
                (K always, V only for tiles some head keeps) against 8 TB/s
@@ -76,8 +79,10 @@ def parse():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-masked", action="store_true", help="skip the block-sparse prefill leg")
+    ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
-    ap.add_argument("--only", choices=["prefill", "prefill_masked", "decode_gqa", "decode_mla", "copy"],
+    ap.add_argument("--only", choices=["prefill", "prefill_masked", "backward", "decode_gqa",
+                                       "decode_mla", "copy"],
                     help="launch only this kernel --steps times (for rocprofv3 counter passes)")
     return ap.parse_args()
 
@@ -227,6 +232,55 @@ def bench_prefill_masked(args, dense_ms):
     return rows
 
 
+def backward_inputs(w, lam, gain):
+    """Forward on the GPU (its mask, lse and bf16 output feed the backward) and a
+    seeded bf16 dout."""
+    import numpy as np
+    import torch
+    from block_sparse_long_skip_amd import attention as A
+    from block_sparse_long_skip_amd import synth
+
+    inp = synth.make_inputs(w.with_gain(gain))
+    q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    del inp
+    fwd = A.prefill(q, k, v, lam, causal=True, br=w.br, bc=w.bc)
+    g = np.random.default_rng(7).standard_normal((w.B, w.Hq, w.Nq, w.dv)).astype(np.float32)
+    dout = torch.from_numpy(g).to(torch.bfloat16).cuda()
+    return q, k, v, fwd, dout
+
+
+def bench_backward(args):
+    """The prefill backward (dq, dk, dv with the forward's mask held fixed) on the
+    bench layer: algorithmic TFLOP/s = 5 products of 2 Br Bc d FLOPs per kept
+    tile (S recomputed, dP, dV, dK, dQ) over the call time."""
+    import torch
+    from block_sparse_long_skip_amd import attention as A
+    from block_sparse_long_skip_amd import synth
+
+    w = synth.WORKLOADS[2]
+    rows = []
+    for gain, lam in ((1.0, args.lam), (6.0, 1e-2)):
+        log(f"[bench] backward inputs gain {gain} lam {lam}")
+        q, k, v, fwd, dout = backward_inputs(w, lam, gain)
+        ws = torch.empty(max(1, w.B * w.Hq * w.Nq * 4), dtype=torch.uint8, device="cuda")
+        call = lambda: A.prefill_backward(q, k, v, fwd.out, dout, fwd.lse, fwd.mask, causal=True,
+                                          workspace=ws)
+        ms, _, _ = time_calls(call, max(3, args.steps // 4), max(args.warmup, 2))
+        kept = fwd.stats[..., 1].double().sum().item()
+        flops = 5 * 2.0 * w.br * w.bc * w.d * kept
+        dense = 2.5 * synth.dense_equivalent_flops(w)  # 5 products of 2 d FLOPs per visible pair
+        tf = flops / (ms * 1e-3) / 1e12
+        rows.append(dict(gain=gain, lam=lam, ms=round(ms, 4), kept_tiles=int(kept),
+                         skip_fraction=round(fwd.skip_fraction, 4),
+                         algorithmic_tflops=round(tf, 2), frac_mfma=round(tf / PEAK_BF16_TFLOPS, 4),
+                         dense_equiv_tflops=round(dense / (ms * 1e-3) / 1e12, 2)))
+        log(f"[bench]   backward gain {gain} lam {lam}: {ms:.3f} ms {tf:.0f} TFLOP/s "
+            f"skip {fwd.skip_fraction:.3f}")
+        del q, k, v, fwd, dout, ws
+        torch.cuda.empty_cache()
+    return rows
+
+
 def bench_decode(args):
     import torch
     from block_sparse_long_skip_amd import attention as A
@@ -332,6 +386,14 @@ def only(args):
         torch.cuda.synchronize()
         log(f"[bench] copied {n} bytes x {args.steps}")
         return
+    if args.only == "backward":
+        w = synth.WORKLOADS[2]
+        q, k, v, fwd, dout = backward_inputs(w, args.lam, 1.0)
+        for _ in range(args.steps):
+            A.prefill_backward(q, k, v, fwd.out, dout, fwd.lse, fwd.mask, causal=True)
+        torch.cuda.synchronize()
+        log(f"[bench] launched backward x {args.steps}")
+        return
     cid = {"prefill": 2, "prefill_masked": 2, "decode_gqa": 3, "decode_mla": 5}[args.only]
     w = synth.WORKLOADS[cid]
     inp = synth.make_inputs(w)
@@ -372,6 +434,7 @@ def main():
     pre, w = bench_prefill(args)
     dense_ms = next((x["ms"] for x in pre["sweep"] if x["gain"] == 1.0 and x["lam"] == 0.0), None)
     masked = None if args.no_masked or dense_ms is None else bench_prefill_masked(args, dense_ms)
+    backward = None if args.no_backward else bench_backward(args)
     decode = None if args.no_decode else bench_decode(args)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, w)
     line = {
@@ -394,6 +457,7 @@ def main():
         "cpu_baseline": cpu,
         "lambda_sweep": pre["sweep"],
         "block_sparse_prefill": masked,
+        "prefill_backward": backward,
         "decode": decode,
         "wall_s": round(time.perf_counter() - t_start, 1),
     }

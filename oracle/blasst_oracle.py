@@ -45,6 +45,9 @@ notes of the repository):
   and its (query tile, key tile) block is in the caller's set; the skip rule
   then runs over the set's tiles only, so "tile 0" is the first tile of the
   set that the query tile visits. Rows that see nothing output zero, lse -inf.
+* Two-pass variant (a reply in the digg thread): the tile map comes from the
+  skip rule on scores of MXFP4-quantized q and k (OCP MX v1.0), then exact
+  attention runs over the kept tiles; see the section at the end.
 
 Arithmetic is float64 throughout; inputs are whatever float values the caller
 passes (bf16 workloads pass the exact bf16 values, widened).
@@ -438,9 +441,131 @@ def masked_dense_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, keep: np
     return (p @ v) / den, (mx + np.log(den))[:, 0]
 
 
+# --------------------------------------------------------------------------- two-pass variant
+#
+# The digg thread suggests a cheaper first pass (one commenter's reply to the
+# authors): recompute q.k in 4-bit precision only to find the maxima (no
+# exponentials are needed there), fix the sparsity map from them, then gather
+# the kept blocks and compute attention over them. Readings taken:
+# * "4-bit" is MXFP4 from the OCP Microscaling Formats (MX) Specification
+#   v1.0: FP4 E2M1 elements, one E8M0 power-of-two scale per block of 32
+#   consecutive elements along the feature axis (here d_qk).
+# * The map is the skip rule itself (blasst_rows) run on the scores of the
+#   dequantized q and k, with the same scale and tiles.
+# * The second pass is exact softmax attention over the kept tiles only:
+#   block-sparse prefill with lambda = 0 and the kept tiles as the set.
+
+MX_BLOCK = 32
+E2M1_MAGNITUDES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])  # code & 7 -> magnitude
+E2M1_EMAX = 2          # exponent of the largest normal, 6 = 1.5 * 2^2
+E2M1_MAX = 6.0
+E8M0_BIAS = 127
+
+
+def round_to_e2m1(a: np.ndarray) -> np.ndarray:
+    """Nearest FP4 E2M1 magnitude to a >= 0, ties to the even code, larger
+    values clamped to the largest normal (6).
+
+    The spacing of E2M1 is 0.5 below 2 (subnormal 0.5 included), 1 in [2, 4)
+    and 2 in [4, 8); np.rint rounds half to even.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    _, ex = np.frexp(a)                       # a = f * 2^ex with f in [0.5, 1)
+    e = np.clip(ex - 1, 0, E2M1_EMAX)         # binade exponent; below 1 the subnormal spacing
+    ulp = np.ldexp(0.5, e)                    # 2^(e - 1): one mantissa bit
+    return np.minimum(np.rint(a / ulp) * ulp, E2M1_MAX)
+
+
+def mx_quantize_fp4(x: np.ndarray) -> tuple:
+    """MXFP4 quantization along the last axis (OCP MX v1.0, conversion of a
+    block of scalar floats to an MX block).
+
+    Per block of 32: shared exponent = floor(log2(max |x|)) - emax_elem,
+    clamped to the E8M0 range [-127, 127] (an all-zero block takes -127);
+    each element is x / 2^shared rounded to E2M1 (round_to_e2m1), the sign
+    copied from x. Returns (codes uint8 [..., d] with sign in bit 3 and the
+    magnitude index in bits 0-2, scales uint8 [..., d / 32] = shared + 127).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    if d % MX_BLOCK:
+        raise ValueError("the feature size must be a multiple of 32")
+    blk = x.reshape(*x.shape[:-1], d // MX_BLOCK, MX_BLOCK)
+    amax = np.abs(blk).max(axis=-1)
+    _, ex = np.frexp(amax)
+    shared = np.where(amax > 0, ex - 1 - E2M1_EMAX, -E8M0_BIAS)
+    shared = np.clip(shared, -E8M0_BIAS, E8M0_BIAS)
+    mag = round_to_e2m1(np.abs(blk) / np.ldexp(1.0, shared)[..., None])
+    code = np.searchsorted(E2M1_MAGNITUDES, mag).astype(np.uint8)
+    code |= (np.signbit(blk).astype(np.uint8) << 3)
+    return code.reshape(x.shape), (shared + E8M0_BIAS).astype(np.uint8)
+
+
+def mx_dequantize_fp4(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """Values of MXFP4 codes: sign * E2M1 magnitude * 2^(scale - 127)."""
+    codes = np.asarray(codes)
+    mag = E2M1_MAGNITUDES[codes & 7]
+    sign = np.where(codes & 8, -1.0, 1.0)
+    x = np.ldexp(1.0, np.asarray(scales, dtype=np.int64) - E8M0_BIAS)
+    return sign * mag * np.repeat(x, MX_BLOCK, axis=-1)
+
+
+def twopass_tile(q: np.ndarray, k: np.ndarray, v: np.ndarray, qd: np.ndarray, kd: np.ndarray,
+                 b: int, hq: int, i: int, lam: float, causal: bool, br: int, bc: int,
+                 scale: Optional[float] = None) -> tuple:
+    """One (batch, query head, query tile) of the two-pass variant.
+
+    qd, kd: the MXFP4-dequantized q and k. Returns (pre, r): pre is the skip
+    rule on the dequantized scores (its mask and gaps are the pass-1 map); r is
+    exact attention of q, k, v over pre's kept tiles.
+    """
+    B, Hq, nq, d = q.shape
+    kvh = hq // (Hq // k.shape[1])
+    if scale is None:
+        scale = default_scale(d)
+    pre = prefill_tile(qd, kd, v, b, hq, i, lam, causal, br, bc, scale)
+    r0, r1 = i * br, min((i + 1) * br, nq)
+    r = block_sparse_rows(q[b, hq, r0:r1], k[b, kvh], v[b, kvh], pre.mask == MASK_KEPT, 0.0,
+                          causal, nq, r0, bc, scale)
+    return pre, r
+
+
+def prefill_twopass(q: np.ndarray, k: np.ndarray, v: np.ndarray, lam: float, causal: bool,
+                    br: int, bc: int, scale: Optional[float] = None) -> OracleResult:
+    """Whole two-pass prefill call. mask, gap and stats are the pass-1 map's
+    (gap on the dequantized scores); out and lse are the exact attention over
+    the kept tiles."""
+    B, Hq, nq, d = q.shape
+    nk, dv = k.shape[2], v.shape[3]
+    if causal and nq > nk:
+        raise ValueError("causal prefill needs Nq <= Nk")
+    qd = mx_dequantize_fp4(*mx_quantize_fp4(q))
+    kd = mx_dequantize_fp4(*mx_quantize_fp4(k))
+    nqt, nkt = -(-nq // br), -(-nk // bc)
+    out = np.zeros((B, Hq, nq, dv))
+    lse = np.full((B, Hq, nq), -np.inf)
+    mask = np.full((B, Hq, nqt, nkt), MASK_NOT_VISITED, dtype=np.uint8)
+    gap = np.full((B, Hq, nqt, nkt), np.nan)
+    stats = np.zeros((B, Hq, 2), dtype=np.int64)
+    for b in range(B):
+        for hq in range(Hq):
+            for i in range(nqt):
+                pre, r = twopass_tile(q, k, v, qd, kd, b, hq, i, lam, causal, br, bc, scale)
+                r0 = i * br
+                out[b, hq, r0:r0 + r.out.shape[0]] = r.out
+                lse[b, hq, r0:r0 + r.out.shape[0]] = r.lse
+                mask[b, hq, i] = pre.mask
+                gap[b, hq, i] = pre.gap
+            stats[b, hq, 0] = int((mask[b, hq] != MASK_NOT_VISITED).sum())
+            stats[b, hq, 1] = int((mask[b, hq] == MASK_KEPT).sum())
+    return OracleResult(out, lse, mask, gap, stats)
+
+
 __all__ = [
     "threshold", "default_scale", "visible", "blasst_rows", "prefill_tile", "prefill",
     "block_sparse_rows", "prefill_masked", "prefill_backward",
+    "round_to_e2m1", "mx_quantize_fp4", "mx_dequantize_fp4", "twopass_tile", "prefill_twopass",
+    "MX_BLOCK", "E2M1_MAGNITUDES",
     "decode_row", "decode", "naive_attention", "expand_tile_mask", "masked_dense_attention",
     "OracleResult", "TileRowResult", "MASK_SKIPPED", "MASK_KEPT", "MASK_NOT_VISITED",
 ]

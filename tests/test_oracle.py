@@ -532,11 +532,142 @@ def pin_backward_finite_difference(orc):
             assert abs((lp - lm) / (2 * hstep) - grad[idx]) < 1e-6, idx
 
 
+def pin_mxfp4_golden(orc):
+    """Hand-derived MXFP4 blocks (tests/golden/mxfp4_blocks.json)."""
+    for blk in _load("mxfp4_blocks.json")["blocks"]:
+        codes, scales = orc.mx_quantize_fp4(np.array([blk["values"]]))
+        assert codes[0].tolist() == blk["codes"], blk["derivation"]
+        assert int(scales[0, 0]) == blk["scale"], blk["derivation"]
+
+
+def _mx_brute(x):
+    """One MXFP4 block by exhaustive search: the shared exponent found by
+    stepping powers of two, each element the nearest of the 8 magnitudes times
+    2^shared (ties to the even code), sign copied."""
+    amax = max(abs(v) for v in x)
+    if amax == 0:
+        e = -127
+    else:
+        e = 0
+        while 2.0 ** (e + 1) <= amax:
+            e += 1
+        while 2.0 ** e > amax:
+            e -= 1
+        e = min(max(e - 2, -127), 127)
+    X = 2.0 ** e
+    mags = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    codes = []
+    for v in x:
+        dist = [abs(abs(v) - m * X) for m in mags]
+        best = min(dist)
+        cands = [c for c in range(8) if dist[c] == best]
+        c = cands[0] if len(cands) == 1 else [c for c in cands if c % 2 == 0][0]
+        codes.append(c | (8 if math.copysign(1.0, v) < 0 else 0))
+    return codes, e + 127
+
+
+def pin_mxfp4_brute_force(orc):
+    """Random blocks over many binades, with planted exact ties, against the
+    exhaustive search; the dequantized values lie within half a spacing."""
+    rng = np.random.default_rng(21)
+    grid_mid = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0]
+    for trial in range(300):
+        e = int(rng.integers(-140, 120))
+        x = rng.standard_normal(32) * 2.0 ** e
+        if trial % 3 == 0:   # exact midpoints of the grid at the block's scale
+            amax_e = int(rng.integers(-20, 20))
+            x = np.array([rng.choice(grid_mid) * rng.choice([-1, 1]) for _ in range(32)]) * 2.0 ** amax_e
+            x[0] = 4.0 * 2.0 ** amax_e
+        if trial % 7 == 0:
+            x[rng.integers(0, 32, 5)] = 0.0
+        codes, scales = orc.mx_quantize_fp4(x[None])
+        bc, bs = _mx_brute(x.tolist())
+        assert codes[0].tolist() == bc, trial
+        assert int(scales[0, 0]) == bs, trial
+    # a row of several blocks quantizes block by block
+    x = rng.standard_normal((3, 128)) * np.repeat(2.0 ** rng.integers(-8, 8, (3, 4)), 32, axis=1)
+    codes, scales = orc.mx_quantize_fp4(x)
+    for r in range(3):
+        for blk in range(4):
+            bc, bs = _mx_brute(x[r, 32 * blk:32 * blk + 32].tolist())
+            assert codes[r, 32 * blk:32 * blk + 32].tolist() == bc
+            assert int(scales[r, blk]) == bs
+    deq = orc.mx_dequantize_fp4(codes, scales)
+    X = np.repeat(2.0 ** (scales.astype(np.int64) - 127), 32, axis=1)
+    a = np.abs(x) / X   # in [0, 8): half the E2M1 spacing, or the clamp above 6
+    half = np.select([a >= 6, a >= 4, a >= 2], [a - 6, 1.0, 0.5], 0.25)
+    assert (np.abs(deq - x) <= half * X * (1 + 1e-12)).all()
+
+
+def _on_grid(rng, shape):
+    """Values that MXFP4 represents exactly: each block of 32 holds a magnitude
+    4 or 6 times its power of two, so the block's shared exponent is that power."""
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    x = rng.choice(mags, size=shape) * rng.choice([-1.0, 1.0], size=shape)
+    blk = x.reshape(*shape[:-1], shape[-1] // 32, 32)
+    blk[..., 0] = rng.choice([4.0, -6.0], size=blk.shape[:-1])
+    pw = 2.0 ** rng.integers(-3, 2, size=blk.shape[:-1])
+    return (blk * pw[..., None]).reshape(shape)
+
+
+def pin_twopass_on_grid(orc):
+    """When q and k are exactly MXFP4-representable, the pre-pass sees the exact
+    scores, so the two-pass result is the one-pass result."""
+    rng = np.random.default_rng(22)
+    for (Hq, Hkv, Nq, Nk, br, bc, causal) in [(2, 1, 40, 70, 8, 8, True), (2, 2, 33, 50, 5, 7, False)]:
+        q = _on_grid(rng, (1, Hq, Nq, 32))
+        k = _on_grid(rng, (1, Hkv, Nk, 32))
+        k[:, :, ::9] = np.abs(k[:, :, ::9])  # some keys align with positive queries
+        q = np.abs(q) * np.where(rng.random(q.shape) < 0.8, 1.0, -1.0)
+        v = rng.standard_normal((1, Hkv, Nk, 8))
+        assert np.array_equal(orc.mx_dequantize_fp4(*orc.mx_quantize_fp4(q)), q)
+        n_dropped = 0
+        for lam in (0.0, 1e-2, 0.3):
+            r1 = orc.prefill(q, k, v, lam, causal, br, bc)
+            r2 = orc.prefill_twopass(q, k, v, lam, causal, br, bc)
+            assert np.array_equal(r1.mask, r2.mask)
+            assert np.array_equal(r1.stats, r2.stats)
+            assert np.abs(r1.out - r2.out).max() < 1e-12
+            assert np.abs(r1.lse - r2.lse).max() < 1e-12
+            n_dropped += int((r1.mask == 0).sum())
+        assert n_dropped > 0, "fixture must exercise dropped tiles"
+
+
+def pin_twopass_map_and_output(orc):
+    """The map is the closed-form prefix-max rule on the dequantized scores
+    (differing from the exact scores' map on this fixture), and the output is
+    softmax over the kept tiles (torch SDPA, float64, element mask)."""
+    rng = np.random.default_rng(23)
+    n_diff = n_dropped = 0
+    for (Hq, Hkv, Nq, Nk, br, bc, causal) in [(2, 1, 64, 96, 16, 8, True), (1, 1, 30, 45, 7, 5, False)]:
+        q, k, v = _rand_case(rng, 1, Hq, Hkv, Nq, Nk, 64, 16, plant=4.0)
+        qd = orc.mx_dequantize_fp4(*orc.mx_quantize_fp4(q))
+        kd = orc.mx_dequantize_fp4(*orc.mx_quantize_fp4(k))
+        sc = 1 / math.sqrt(64)
+        for lam in (1e-2, 0.1, 0.3):
+            r = orc.prefill_twopass(q, k, v, lam, causal, br, bc)
+            assert (r.mask == _prefix_max_closed_form(qd, kd, lam, causal, br, bc, sc)).all()
+            exact = _prefix_max_closed_form(q, k, lam, causal, br, bc, sc)
+            n_diff += int((exact != r.mask).sum())
+            n_dropped += int((r.mask == 0).sum())
+            G = Hq // Hkv
+            for h in range(Hq):
+                keep = orc.expand_tile_mask(r.mask[0, h], br, bc, Nq, Nk)
+                allowed = keep & orc.visible(Nq, Nk, causal)
+                ref = _sdpa(q[0, h][None], k[0, h // G][None], v[0, h // G][None], False, sc,
+                            np.where(allowed, 0.0, -np.inf)[None])[0]
+                assert np.abs(r.out[0, h] - ref).max() < 1e-12
+            assert (r.stats[..., 1] == (r.mask == 1).sum(axis=(2, 3))).all()
+    assert n_diff > 0, "fixture must make the 4-bit map differ from the exact one"
+    assert n_dropped > 0
+
+
 PINS = [pin_hand_example, pin_row_aggregation, pin_tie, pin_causal_visibility,
         pin_lambda0_sdpa, pin_bottom_right_causal, pin_masked_sdpa, pin_closed_form_mask,
         pin_brute_force, pin_decode_sdpa, pin_block_sparse_sdpa, pin_block_sparse_kept,
         pin_block_sparse_full_set, pin_block_sparse_brute, pin_backward_autograd,
-        pin_backward_finite_difference]
+        pin_backward_finite_difference, pin_mxfp4_golden, pin_mxfp4_brute_force,
+        pin_twopass_on_grid, pin_twopass_map_and_output]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda p: p.__name__)
@@ -655,6 +786,12 @@ MUTATIONS = {
     "bwd_unnormalised_p": ("p = np.where(live, e / np.where(live, den, 1.0), 0.0)",
                            "p = np.where(live, e, 0.0)"),
     "bwd_dk_uses_dp": ("dk[b, kvh] += scale * (ds.T @ q[b, hq])", "dk[b, kvh] += scale * (dp.T @ q[b, hq])"),
+    "mx_scale_exponent_off_by_one": ("ex - 1 - E2M1_EMAX, -E8M0_BIAS)", "ex - E2M1_EMAX, -E8M0_BIAS)"),
+    "mx_round_half_up": ("np.rint(a / ulp) * ulp", "np.floor(a / ulp + 0.5) * ulp"),
+    "mx_no_clamp": ("np.minimum(np.rint(a / ulp) * ulp, E2M1_MAX)", "np.rint(a / ulp) * ulp"),
+    "mx_sign_dropped": ("code |= (np.signbit(blk).astype(np.uint8) << 3)", "code |= 0"),
+    "twopass_decides_on_exact_scores": ("pre = prefill_tile(qd, kd, v,", "pre = prefill_tile(q, k, v,"),
+    "twopass_pass2_over_visible": ("pre.mask == MASK_KEPT, 0.0,", "pre.mask != MASK_NOT_VISITED, 0.0,"),
 }
 
 

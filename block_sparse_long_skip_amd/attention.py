@@ -30,7 +30,9 @@ STATUS = {
 
 # Every symbol include/blasst.h declares.
 EXPORTED = ("blasst_attn_prefill", "blasst_attn_prefill_masked", "blasst_attn_prefill_backward",
-            "blasst_prefill_backward_workspace_size", "blasst_attn_decode",
+            "blasst_prefill_backward_workspace_size", "blasst_quantize_mxfp4",
+            "blasst_attn_prefill_twopass", "blasst_prefill_twopass_workspace_size",
+            "blasst_attn_decode",
             "blasst_decode_workspace_size", "blasst_status_string", "blasst_last_error",
             "blasst_version")
 
@@ -89,6 +91,20 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                                            ctypes.c_int, ctypes.c_int,
                                                            ctypes.c_int,
                                                            ctypes.POINTER(ctypes.c_size_t)]
+    lib.blasst_quantize_mxfp4.restype = ctypes.c_int
+    lib.blasst_quantize_mxfp4.argtypes = [vp, ctypes.POINTER(ctypes.c_int64), ctypes.c_int32,
+                                          ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                          ctypes.c_int, u8p, u8p, vp]
+    lib.blasst_attn_prefill_twopass.restype = ctypes.c_int
+    lib.blasst_attn_prefill_twopass.argtypes = [vp, vp, vp, vp, u8p, fp, i64p, ctypes.POINTER(Shape),
+                                                ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                                ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                                ctypes.c_int, vp, ctypes.c_size_t, vp]
+    lib.blasst_prefill_twopass_workspace_size.restype = ctypes.c_int
+    lib.blasst_prefill_twopass_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int,
+                                                          ctypes.c_int, ctypes.c_int,
+                                                          ctypes.c_int,
+                                                          ctypes.POINTER(ctypes.c_size_t)]
     lib.blasst_attn_decode.restype = ctypes.c_int
     lib.blasst_attn_decode.argtypes = [vp, vp, vp, vp, u8p, fp, i64p, ctypes.POINTER(Shape),
                                        ctypes.c_int, ctypes.c_int, ctypes.c_float,
@@ -264,6 +280,70 @@ def prefill_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, out: tor
     return dq, dk, dv
 
 
+def quantize_mxfp4(x: torch.Tensor) -> tuple:
+    """MXFP4 codes and E8M0 scales of a bf16 [d0, d1, n, d] tensor (features
+    contiguous): codes uint8 [d0, d1, n, d / 2] (two per byte, the even
+    feature in the low nibble), scales uint8 [d0, d1, n, d / 32]."""
+    lib = load_library()
+    _require_device(x)
+    d0, d1, n, d = x.shape
+    codes = torch.empty((d0, d1, n, d // 2), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((d0, d1, n, max(d // 32, 0)), dtype=torch.uint8, device=x.device)
+    xs = (ctypes.c_int64 * 3)(*_strides3(x))
+    _check(lib.blasst_quantize_mxfp4(_ptr(x), xs, d0, d1, n, d, _dtype_code(x.dtype), _ptr(codes),
+                                     _ptr(scales), _stream(x.device)))
+    return codes, scales
+
+
+def prefill_twopass_workspace_size(B: int, Hq: int, Hkv: int, Nq: int, Nk: int, d: int = 128,
+                                   dv: int = 128, causal: bool = True, br: int = 128,
+                                   bc: int = 64, dtype: torch.dtype = torch.bfloat16) -> int:
+    """Bytes of device workspace blasst_attn_prefill_twopass needs."""
+    lib = load_library()
+    z = (0, 0, 0)
+    sh = Shape(B, Hq, Hkv, Nq, Nk, d, dv, z, z, z, z)
+    n = ctypes.c_size_t(0)
+    _check(lib.blasst_prefill_twopass_workspace_size(ctypes.byref(sh), _dtype_code(dtype),
+                                                     int(bool(causal)), int(br), int(bc),
+                                                     ctypes.byref(n)))
+    return n.value
+
+
+def prefill_twopass(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, lam: float,
+                    causal: bool = True, br: int = 128, bc: int = 64,
+                    scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+                    out_dtype: Optional[torch.dtype] = None, want_mask: bool = True,
+                    want_lse: bool = True, want_stats: bool = True,
+                    workspace: Optional[torch.Tensor] = None) -> AttnResult:
+    """Two-pass prefill: the tile map from the skip rule on MXFP4 scores, then
+    exact attention over the kept tiles. ``mask`` of the result is that map."""
+    lib = load_library()
+    _require_device(q, k, v, out, workspace)
+    B, Hq, Nq, d = q.shape
+    Hkv, Nk, dv = k.shape[1], k.shape[2], v.shape[3]
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, Hq, Nq, dv), dtype=out_dtype or q.dtype, device=dev)
+    nqt, nkt = -(-Nq // br), -(-Nk // bc)
+    mask = torch.empty((B, Hq, nqt, nkt), dtype=torch.uint8, device=dev) if want_mask else None
+    lse = torch.empty((B, Hq, Nq), dtype=torch.float32, device=dev) if want_lse else None
+    stats = torch.empty((B, Hq, 2), dtype=torch.int64, device=dev) if want_stats else None
+    sh = Shape(B, Hq, Hkv, Nq, Nk, d, dv, _strides3(q), _strides3(k), _strides3(v), _strides3(out))
+    n = ctypes.c_size_t(0)
+    _check(lib.blasst_prefill_twopass_workspace_size(ctypes.byref(sh), _dtype_code(q.dtype),
+                                                     int(bool(causal)), int(br), int(bc),
+                                                     ctypes.byref(n)))
+    if workspace is None:
+        workspace = _workspace(n.value, dev)
+    st = lib.blasst_attn_prefill_twopass(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(out), _ptr(mask), _ptr(lse), _ptr(stats), ctypes.byref(sh),
+        _dtype_code(q.dtype), _dtype_code(out.dtype), float(lam), float(scale) if scale else 0.0,
+        int(bool(causal)), int(br), int(bc), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(dev))
+    _check(st)
+    return AttnResult(out, mask, lse, stats)
+
+
 def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor], lam: float,
            bc: int = 64, scale: Optional[float] = None, dv: Optional[int] = None,
            out: Optional[torch.Tensor] = None, out_dtype: Optional[torch.dtype] = None,
@@ -333,5 +413,6 @@ def default_scale(d: int) -> float:
     return 1.0 / math.sqrt(d)
 
 
-__all__ = ["prefill", "prefill_masked", "prefill_backward", "decode", "decode_workspace_size", "load_library", "Shape", "BlasstError", "AttnResult",
+__all__ = ["prefill", "prefill_masked", "prefill_backward", "quantize_mxfp4",
+           "prefill_twopass", "prefill_twopass_workspace_size", "decode", "decode_workspace_size", "load_library", "Shape", "BlasstError", "AttnResult",
            "EXPORTED", "LIB_PATH", "STATUS"]

@@ -21,8 +21,8 @@ ROOT = os.path.dirname(HERE)
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libblasst.so")
 
-SOURCES = ["api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "backward_bf16.hip", "decode.hip",
-           "decode_mla.hip"]
+SOURCES = ["api.cpp", "prefill_f32.hip", "prefill_bf16.hip", "backward_bf16.hip", "twopass.hip",
+           "decode.hip", "decode_mla.hip"]
 ARCH = "gfx950"
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 # Per-source device flags. The latent-cache decode kernel keeps its output

@@ -19,6 +19,8 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeArgs& a, void* workspace, hipStream_t stream);
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream);
+hipError_t launch_mx_quantize_fp4(const MxQuantArgs& a, hipStream_t stream);
+hipError_t launch_twopass_map(const TwoPassMapArgs& a, hipStream_t stream);
 size_t decode_mla_workspace_bytes(int B, int Hq, int Hkv, int G, int nkt);
 
 __global__ void zero_i64_kernel(int64_t* p, int64_t n) {
@@ -90,12 +92,13 @@ blasst_status_t zero_stats(int64_t* stats, int64_t n, hipStream_t st) {
 }
 
 // Both prefill entry points; block_mask is NULL for plain prefill.
-blasst_status_t run_prefill(const void* q, const void* k, const void* v,
-                            const uint8_t* block_mask, const int64_t* block_mask_stride,
-                            void* out, uint8_t* mask_out, float* lse_out, int64_t* stats_out,
-                            const blasst_shape_t* shape, blasst_dtype_t dtype,
-                            blasst_dtype_t out_dtype, float lambda, float scale, int causal,
-                            int br, int bc, void* stream) {
+// Validates a prefill call and fills its kernel arguments; launches nothing.
+blasst_status_t prepare_prefill(const void* q, const void* k, const void* v,
+                                const uint8_t* block_mask, const int64_t* block_mask_stride,
+                                void* out, uint8_t* mask_out, float* lse_out, int64_t* stats_out,
+                                const blasst_shape_t* shape, blasst_dtype_t dtype,
+                                blasst_dtype_t out_dtype, float lambda, float scale, int causal,
+                                int br, int bc, blasst::PrefillArgs* args, bool* use_f32) {
   blasst_status_t st0;
   if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
   if (!q || !k || !v || !out) return fail(BLASST_E_NULL, "q, k, v and out are required");
@@ -166,7 +169,24 @@ blasst_status_t run_prefill(const void* q, const void* k, const void* v,
   a.scale = sc;
   a.scale_log2 = sc * blasst::kLog2e;
   a.thr_raw = raw_threshold(lambda, sc);
+  *args = a;
+  *use_f32 = f32;
+  return BLASST_OK;
+}
 
+blasst_status_t run_prefill(const void* q, const void* k, const void* v,
+                            const uint8_t* block_mask, const int64_t* block_mask_stride,
+                            void* out, uint8_t* mask_out, float* lse_out, int64_t* stats_out,
+                            const blasst_shape_t* shape, blasst_dtype_t dtype,
+                            blasst_dtype_t out_dtype, float lambda, float scale, int causal,
+                            int br, int bc, void* stream) {
+  blasst::PrefillArgs a;
+  bool f32 = false;
+  blasst_status_t st = prepare_prefill(q, k, v, block_mask, block_mask_stride, out, mask_out,
+                                       lse_out, stats_out, shape, dtype, out_dtype, lambda, scale,
+                                       causal, br, bc, &a, &f32);
+  if (st != BLASST_OK) return st;
+  const blasst_shape_t& s = *shape;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
   st = zero_stats(stats_out, (int64_t)s.batch * s.heads_q * 2, hs);
   if (st != BLASST_OK) return st;
@@ -448,6 +468,156 @@ blasst_status_t blasst_attn_prefill_backward(
   if (s.batch == 0) return ok();
   return hip_status(blasst::launch_backward_bf16(a, reinterpret_cast<hipStream_t>(stream)),
                     "backward launch");
+}
+
+}  // extern "C"
+
+namespace {
+
+// Byte offsets of the two-pass workspace segments, each 256-byte aligned.
+struct TwoPassLayout {
+  size_t qc, qs, kc, ks, map, total;
+};
+
+size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+TwoPassLayout twopass_layout(const blasst_shape_t& s, int br, int bc) {
+  const size_t qrows = (size_t)s.batch * s.heads_q * s.len_q;
+  const size_t krows = (size_t)s.batch * s.heads_kv * s.len_kv;
+  const size_t nqt = ((size_t)s.len_q + br - 1) / br, nkt = ((size_t)s.len_kv + bc - 1) / bc;
+  TwoPassLayout L;
+  L.qc = 0;
+  L.qs = L.qc + align256(qrows * (s.d_qk / 2));
+  L.kc = L.qs + align256(qrows * (s.d_qk / 32));
+  L.ks = L.kc + align256(krows * (s.d_qk / 2));
+  L.map = L.ks + align256(krows * (s.d_qk / 32));
+  L.total = L.map + align256((size_t)s.batch * s.heads_q * nqt * nkt);
+  return L;
+}
+
+// The two-pass call supports exactly the block-sparse prefill's configuration.
+blasst_status_t check_twopass(const blasst_shape_t& s, blasst_dtype_t dtype, int causal, int br,
+                              int bc) {
+  if (s.batch < 0 || s.heads_q < 1 || s.heads_kv < 1 || s.len_q < 0 || s.len_kv < 1 ||
+      s.d_qk < 1 || s.d_v < 1)
+    return fail(BLASST_E_SHAPE, "sizes out of range (B=%d Hq=%d Hkv=%d Nq=%d Nk=%d d=%d dv=%d)",
+                s.batch, s.heads_q, s.heads_kv, s.len_q, s.len_kv, s.d_qk, s.d_v);
+  if (dtype != BLASST_FP32 && dtype != BLASST_BF16)
+    return fail(BLASST_E_DTYPE, "unknown dtype %d", (int)dtype);
+  if (dtype != BLASST_BF16 || s.d_qk != 128 || s.d_v != 128 || br != 128 || bc != 64)
+    return fail(BLASST_E_UNSUPPORTED,
+                "no two-pass kernel for dtype=%d d_qk=%d d_v=%d br=%d bc=%d (supported: bf16 "
+                "128/128 128x64)",
+                (int)dtype, s.d_qk, s.d_v, br, bc);
+  (void)causal;
+  return BLASST_OK;
+}
+
+blasst_status_t check_workspace(const void* ws, size_t bytes, size_t need) {
+  if (need == 0) return BLASST_OK;
+  if (!ws) return fail(BLASST_E_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (bytes < need)
+    return fail(BLASST_E_WORKSPACE, "workspace of %zu bytes is smaller than %zu", bytes, need);
+  if ((reinterpret_cast<uintptr_t>(ws) & 255u) != 0)
+    return fail(BLASST_E_WORKSPACE, "workspace must be 256-byte aligned");
+  return BLASST_OK;
+}
+
+blasst::MxQuantArgs quant_args(const void* x, const int64_t* stride, int d0, int d1, int n, int d,
+                               uint8_t* codes, uint8_t* scales) {
+  blasst::MxQuantArgs a;
+  a.x = x; a.codes = codes; a.scales = scales;
+  a.d0 = d0; a.d1 = d1; a.n = n; a.d = d;
+  a.s0 = stride[0]; a.s1 = stride[1]; a.s2 = stride[2];
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+blasst_status_t blasst_quantize_mxfp4(const void* x, const int64_t x_stride[3], int32_t d0,
+                                      int32_t d1, int32_t n, int32_t d, blasst_dtype_t dtype,
+                                      uint8_t* codes, uint8_t* scales, void* stream) {
+  if (!x || !x_stride || !codes || !scales)
+    return fail(BLASST_E_NULL, "x, x_stride, codes and scales are required");
+  if (d0 < 0 || d1 < 0 || n < 0 || d < 32 || d % 32 != 0)
+    return fail(BLASST_E_SHAPE, "need d0, d1, n >= 0 and d a positive multiple of 32 (got %d %d %d %d)",
+                d0, d1, n, d);
+  if (dtype != BLASST_BF16) return fail(BLASST_E_DTYPE, "MXFP4 quantization takes bf16 input");
+  if (!aligned16(x) || !aligned16(codes)) return fail(BLASST_E_ALIGN, "x and codes must be 16-byte aligned");
+  if (!strides_aligned(x_stride, 3, 2))
+    return fail(BLASST_E_ALIGN, "every stride times the element size must be a multiple of 16");
+  if ((int64_t)d0 * d1 * n * (d / 32) > 0x7fffffffLL * 256LL)
+    return fail(BLASST_E_UNSUPPORTED, "grid too large");
+  const blasst::MxQuantArgs a = quant_args(x, x_stride, d0, d1, n, d, codes, scales);
+  return hip_status(blasst::launch_mx_quantize_fp4(a, reinterpret_cast<hipStream_t>(stream)),
+                    "MXFP4 quantize launch");
+}
+
+blasst_status_t blasst_prefill_twopass_workspace_size(const blasst_shape_t* shape,
+                                                      blasst_dtype_t dtype, int causal, int br,
+                                                      int bc, size_t* bytes) {
+  if (!shape || !bytes) return fail(BLASST_E_NULL, "shape and bytes are required");
+  const blasst_status_t st = check_twopass(*shape, dtype, causal, br, bc);
+  if (st != BLASST_OK) return st;
+  *bytes = twopass_layout(*shape, br, bc).total;
+  return ok();
+}
+
+blasst_status_t blasst_attn_prefill_twopass(const void* q, const void* k, const void* v,
+                                            void* out, uint8_t* mask_out, float* lse_out,
+                                            int64_t* stats_out, const blasst_shape_t* shape,
+                                            blasst_dtype_t dtype, blasst_dtype_t out_dtype,
+                                            float lambda, float scale, int causal, int br, int bc,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream) {
+  if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
+  const blasst_shape_t& s = *shape;
+  blasst_status_t st = check_twopass(s, dtype, causal, br, bc);
+  if (st != BLASST_OK) return st;
+  const TwoPassLayout L = twopass_layout(s, br, bc);
+  // the second pass is the block-sparse prefill over the map; validating it
+  // first covers every pointer, stride and size rule of the inputs and outputs
+  char* ws = static_cast<char*>(workspace);
+  uint8_t* map = mask_out ? mask_out : (ws ? reinterpret_cast<uint8_t*>(ws + L.map) : nullptr);
+  const int nqt = (s.len_q + br - 1) / br, nkt = (s.len_kv + bc - 1) / bc;
+  const int64_t map_stride[3] = {(int64_t)s.heads_q * nqt * nkt, (int64_t)nqt * nkt, nkt};
+  blasst::PrefillArgs a2;
+  bool f32 = false;
+  st = prepare_prefill(q, k, v, map, map_stride, out,
+                       nullptr, lse_out, nullptr, shape, dtype, out_dtype, lambda, scale, causal,
+                       br, bc, &a2, &f32);
+  if (st != BLASST_OK) return st;
+  st = check_workspace(workspace, workspace_bytes, L.total);
+  if (st != BLASST_OK) return st;
+  a2.thr_raw = raw_threshold(0.f, a2.scale);  // exact softmax over the kept tiles
+
+  blasst::TwoPassMapArgs m;
+  m.qc = reinterpret_cast<const uint8_t*>(ws + L.qc);
+  m.qs = reinterpret_cast<const uint8_t*>(ws + L.qs);
+  m.kc = reinterpret_cast<const uint8_t*>(ws + L.kc);
+  m.ks = reinterpret_cast<const uint8_t*>(ws + L.ks);
+  m.map = map;
+  m.stats = stats_out;
+  m.B = s.batch; m.Hq = s.heads_q; m.Hkv = s.heads_kv; m.Nq = s.len_q; m.Nk = s.len_kv;
+  m.nqt = nqt; m.nkt = nkt; m.causal = causal ? 1 : 0;
+  m.thr_raw = raw_threshold(lambda, a2.scale);
+
+  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  st = zero_stats(stats_out, (int64_t)s.batch * s.heads_q * 2, hs);
+  if (st != BLASST_OK) return st;
+  if (s.batch == 0 || s.len_q == 0) return ok();
+  hipError_t e = blasst::launch_mx_quantize_fp4(
+      quant_args(q, s.q_stride, s.batch, s.heads_q, s.len_q, s.d_qk, reinterpret_cast<uint8_t*>(ws + L.qc),
+                 reinterpret_cast<uint8_t*>(ws + L.qs)), hs);
+  if (e == hipSuccess)
+    e = blasst::launch_mx_quantize_fp4(
+        quant_args(k, s.k_stride, s.batch, s.heads_kv, s.len_kv, s.d_qk,
+                   reinterpret_cast<uint8_t*>(ws + L.kc), reinterpret_cast<uint8_t*>(ws + L.ks)), hs);
+  if (e == hipSuccess) e = blasst::launch_twopass_map(m, hs);
+  if (e == hipSuccess) e = blasst::launch_prefill_bf16(a2, hs);
+  return hip_status(e, "two-pass prefill launch");
 }
 
 }  // extern "C"

@@ -70,6 +70,33 @@ struct BackwardArgs {
   float scale, scale_log2;
 };
 
+// Arguments of the MXFP4 quantizer: x [d0, d1, n, d] bf16 with element
+// strides s0..s2 (features contiguous) -> codes [d0 * d1 * n][d / 2] (two
+// elements per byte, the even one in the low nibble) and scales
+// [d0 * d1 * n][d / 32] (E8M0), both contiguous.
+struct MxQuantArgs {
+  const void* x;
+  uint8_t* codes;
+  uint8_t* scales;
+  int d0, d1, n, d;
+  int64_t s0, s1, s2;
+};
+
+// Arguments of the two-pass map kernel (d = 128: 64 code bytes and 4 scale
+// bytes per row, rows ordered as (batch, head, position)).
+struct TwoPassMapArgs {
+  const uint8_t* qc;   // [B * Hq * Nq][64]
+  const uint8_t* qs;   // [B * Hq * Nq][4]
+  const uint8_t* kc;   // [B * Hkv * Nk][64]
+  const uint8_t* ks;   // [B * Hkv * Nk][4]
+  uint8_t* map;        // [B, Hq, nqt, nkt]: 0 dropped, 1 kept, 2 not visited
+  int64_t* stats;      // nullable [B, Hq, 2], zeroed by the launcher
+  int B, Hq, Hkv, Nq, Nk;
+  int nqt, nkt;
+  int causal;
+  float thr_raw;       // ln(lambda) / scale
+};
+
 // Arguments of the decode kernels.
 struct DecodeArgs {
   const void* q;

@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define BLASST_VERSION 220 /* 2.2.0: prefill backward */
+#define BLASST_VERSION 230 /* 2.3.0: two-pass prefill, MXFP4 quantization */
 
 typedef enum blasst_status {
   BLASST_OK = 0,
@@ -170,6 +170,73 @@ blasst_status_t blasst_attn_prefill_masked(const void* q, const void* k, const v
                                            blasst_dtype_t dtype, blasst_dtype_t out_dtype,
                                            float lambda, float scale, int causal, int br, int bc,
                                            void* stream);
+
+/*
+ * MXFP4 quantization, the 4-bit format of the two-pass prefill's max
+ * pre-pass (OCP Microscaling Formats (MX) Specification v1.0: FP4 E2M1
+ * elements sharing one E8M0 scale per block of 32 consecutive features).
+ * Per block: shared = floor(log2 max|x|) - 2, clamped to [-127, 127] (an
+ * all-zero block takes -127); each element is x / 2^shared rounded to the
+ * nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 (ties to the even code, larger values
+ * clamped to 6), with the sign bit of x.
+ *
+ *   x         DEVICE bf16 [d0, d1, n, d], element strides x_stride[0..2]
+ *             (HOST int64[3]), features contiguous; read only
+ *   codes     DEVICE uint8 [d0, d1, n, d / 2], contiguous, written: feature 2j
+ *             of a row in the low nibble of byte j; a code is sign << 3 |
+ *             index of the magnitude in the list above
+ *   scales    DEVICE uint8 [d0, d1, n, d / 32], contiguous, written: shared + 127
+ *   stream    hipStream_t; asynchronous
+ *
+ * d must be a positive multiple of 32; x and codes 16-byte aligned, strides
+ * multiples of 8 elements. Inputs must be finite. dtype must be BLASST_BF16.
+ */
+blasst_status_t blasst_quantize_mxfp4(const void* x, const int64_t x_stride[3], int32_t d0,
+                                      int32_t d1, int32_t n, int32_t d, blasst_dtype_t dtype,
+                                      uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * Two-pass prefill. A reply in the digg thread "BLASST wins Best Paper at
+ * MLSys 2026 ..." proposes a first pass that recomputes q.k in 4-bit only to
+ * find the maxima, then gathering the kept blocks for the real computation.
+ * Pass 1 quantizes q and k to MXFP4 (blasst_quantize_mxfp4, into the
+ * workspace) and runs the skip rule of blasst_attn_prefill on the scores of
+ * the quantized values (scale * q~.k~, same lambda, tiles and conventions),
+ * which gives the tile map. Pass 2 computes exact softmax attention over the
+ * map's kept tiles (the block-sparse prefill with lambda = 0 and the kept
+ * tiles as the set). Decisions therefore follow the 4-bit scores and may
+ * differ from blasst_attn_prefill's; the output is exact given the map.
+ *
+ *   q, k, v, out, lse_out   as for blasst_attn_prefill
+ *   mask_out   nullable: the pass-1 map [B, Hq, ceil(Nq/br), ceil(Nk/bc)]
+ *              (0 dropped, 1 kept, 2 not visited); when NULL the map lives in
+ *              the workspace
+ *   stats_out  nullable [B, Hq, 2] = {visited, kept} of the map
+ *   workspace  DEVICE, 256-byte aligned, at least
+ *              blasst_prefill_twopass_workspace_size bytes; holds the MXFP4
+ *              copies of q and k and the map; its contents do not carry over
+ *              between calls, and overlapping calls must not share it
+ *
+ * Supported (else BLASST_E_UNSUPPORTED): BLASST_BF16, d_qk = d_v = 128,
+ * br = 128, bc = 64, ceil(Nk/64) <= 6144. Validation as for
+ * blasst_attn_prefill_masked, plus BLASST_E_WORKSPACE.
+ */
+blasst_status_t blasst_attn_prefill_twopass(const void* q, const void* k, const void* v,
+                                            void* out, uint8_t* mask_out, float* lse_out,
+                                            int64_t* stats_out, const blasst_shape_t* shape,
+                                            blasst_dtype_t dtype, blasst_dtype_t out_dtype,
+                                            float lambda, float scale, int causal, int br, int bc,
+                                            void* workspace, size_t workspace_bytes,
+                                            void* stream);
+
+/*
+ * Workspace bytes blasst_attn_prefill_twopass needs for this shape. Validates
+ * the size, dtype and tile combination and writes *bytes only on BLASST_OK.
+ * Launches nothing.
+ */
+blasst_status_t blasst_prefill_twopass_workspace_size(const blasst_shape_t* shape,
+                                                      blasst_dtype_t dtype, int causal, int br,
+                                                      int bc, size_t* bytes);
 
 /*
  * Prefill backward: gradients of a bf16 skip-softmax prefill with its tile

@@ -169,6 +169,38 @@ def prefill_masked_tile_parity(res, inp, w: synth.Workload, lam: float, sel: np.
     return t
 
 
+def mxfp4_values(x: np.ndarray) -> np.ndarray:
+    """The oracle's MXFP4 round trip of float values (blocks of 32 along the last axis)."""
+    return oracle.mx_dequantize_fp4(*oracle.mx_quantize_fp4(x))
+
+
+def prefill_twopass_tile_parity(res, inp, w: synth.Workload, lam: float, b: int, h: int, i: int,
+                                tally: Tally, kf=None, vf=None, kd=None):
+    """Compare one (b, h, query tile i) of a GPU two-pass prefill with the oracle:
+    the map against the skip rule on the MXFP4-dequantized q and k (whose gaps
+    define the near-threshold band), the output against exact attention over the
+    kept tiles (the GPU's own kept tiles where the map flipped inside the band).
+    kd: the dequantized keys of the head, when the caller caches them."""
+    kvh = h // (w.Hq // w.Hkv)
+    r0, r1 = i * w.br, min((i + 1) * w.br, w.Nq)
+    q = synth.to_float(inp.q[b, h, r0:r1], w)
+    k = kf if kf is not None else synth.to_float(inp.k[b, kvh], w)
+    v = vf if vf is not None else synth.to_float(inp.v[b, kvh], w)
+    kd = kd if kd is not None else mxfp4_values(k)
+    scale = 1.0 / math.sqrt(w.d)
+    vis = oracle.visible(w.Nq, w.Nk, w.causal, r0, r1 - r0)
+    pre = oracle.blasst_rows(mxfp4_values(q), kd, v, lam, w.bc, vis, scale)
+    gpu_mask = res.mask[b, h, i].cpu().numpy()
+    flips = check_mask_row(gpu_mask, pre.mask, pre.gap, lam, tally, f"b{b} h{h} qtile{i}")
+    kept = gpu_mask if flips.any() else pre.mask
+    t = oracle.block_sparse_rows(q, k, v, (kept == oracle.MASK_KEPT).astype(np.uint8), 0.0,
+                                 w.causal, w.Nq, r0, w.bc, scale)
+    got = from_device(res.out[b, h, r0:r1])
+    got_lse = res.lse[b, h, r0:r1].cpu().numpy().astype(np.float64)
+    tally.add(got - t.out, lse_diff(got_lse, t.lse), t.out)
+    return pre
+
+
 def decode_row_parity(res, q64, k64, v64, lam: float, bc: int, b: int, hq: int, tally: Tally):
     """Compare one (b, hq) decode row. q64 [d]; k64 [Nk,d]; v64 [Nk,dv] (float64)."""
     nk = k64.shape[0]

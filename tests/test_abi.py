@@ -24,7 +24,7 @@ BF16, FP32 = A.BLASST_BF16, A.BLASST_FP32
 def _header_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(blasst_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(blasst_[a-z0-9_]+)\s*\(", src)))
 
 
 def test_exports_every_declared_symbol():
@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
     assert set(declared) == set(A.EXPORTED)
     for name in declared:
         assert hasattr(lib, name), name
-    assert lib.blasst_version() == 220
+    assert lib.blasst_version() == 230
 
 
 def test_status_strings():
@@ -230,6 +230,108 @@ def test_prefill_backward_workspace_size():
     assert n.value >= 2 * 4 * 300 * 4 and n.value % 256 == 0
     assert lib.blasst_prefill_backward_workspace_size(ctypes.byref(sh), FP32, 1, 128, 64,
                                                       ctypes.byref(n)) == 6
+
+
+def _twopass(sh, dtype=BF16, br=128, bc=64, ws=P, ws_bytes=1 << 30, q=P, mask=P, lam=1e-3,
+             scale=0.0, out_dtype=None, causal=1):
+    lib = A.load_library()
+    return lib.blasst_attn_prefill_twopass(q, P, P, P, mask, P, P, ctypes.byref(sh), dtype,
+                                           dtype if out_dtype is None else out_dtype, lam, scale,
+                                           causal, br, bc, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_q", 1), ("f32", 6), ("bad_d", 6), ("bad_tile", 6), ("heads", 2), ("causal_nq_gt_nk", 2),
+    ("no_workspace", 9), ("no_workspace_no_mask", 9), ("small_workspace", 9),
+    ("misaligned_workspace", 9), ("lam", 4), ("scale_inf", 7), ("misaligned_stride", 5),
+    ("too_many_key_tiles", 6), ("bad_out_dtype", 3), ("null_shape", 1),
+])
+def test_prefill_twopass_validation(case, expect):
+    sh = _shape()
+    kw = {}
+    if case == "null_q":
+        kw["q"] = None
+    elif case == "f32":
+        sh = _shape(d=64, dv=64)
+        kw["dtype"], kw["br"] = FP32, 64
+    elif case == "bad_d":
+        sh.d_qk = sh.d_v = 96
+    elif case == "bad_tile":
+        kw["bc"] = 128
+    elif case == "heads":
+        sh.heads_q = 3
+    elif case == "causal_nq_gt_nk":
+        sh.len_q, sh.len_kv = 300, 200
+    elif case == "no_workspace":
+        kw["ws"] = None
+    elif case == "no_workspace_no_mask":
+        kw["ws"], kw["mask"] = None, None
+    elif case == "small_workspace":
+        kw["ws_bytes"] = 16
+    elif case == "misaligned_workspace":
+        kw["ws"] = P + 16
+    elif case == "lam":
+        kw["lam"] = 1.5
+    elif case == "scale_inf":
+        kw["scale"] = math.inf
+    elif case == "misaligned_stride":
+        sh.q_stride[1] += 4
+    elif case == "too_many_key_tiles":
+        sh = _shape(Nq=128, Nk=6144 * 64 + 1)
+    elif case == "bad_out_dtype":
+        kw["out_dtype"] = 7
+    if case == "null_shape":
+        lib = A.load_library()
+        st = lib.blasst_attn_prefill_twopass(P, P, P, P, P, P, P, None, BF16, BF16, 1e-3, 0.0, 1,
+                                             128, 64, P, 1 << 30, None)
+        assert st == expect, _err()
+    else:
+        assert _twopass(sh, **kw) == expect, _err()
+    assert _err() != ""
+
+
+def test_prefill_twopass_workspace_size():
+    lib = A.load_library()
+    n = ctypes.c_size_t(7)
+    sh = _shape(B=2, Hq=4, Hkv=2, Nq=300, Nk=700)
+    assert lib.blasst_prefill_twopass_workspace_size(ctypes.byref(sh), BF16, 1, 128, 64,
+                                                     ctypes.byref(n)) == 0, _err()
+    need = (2 * 4 * 300 * (64 + 4) + 2 * 2 * 700 * (64 + 4) + 2 * 4 * 3 * 11)
+    assert need <= n.value <= need + 5 * 256 and n.value % 256 == 0
+    assert lib.blasst_prefill_twopass_workspace_size(ctypes.byref(sh), BF16, 1, 64, 64,
+                                                     ctypes.byref(n)) == 6
+
+
+@pytest.mark.parametrize("case,expect", [
+    ("null_x", 1), ("null_codes", 1), ("d_not_multiple", 2), ("d_zero", 2), ("negative_n", 2),
+    ("f32", 3), ("misaligned_x", 5), ("misaligned_codes", 5), ("misaligned_stride", 5),
+])
+def test_quantize_mxfp4_validation(case, expect):
+    lib = A.load_library()
+    x, codes, d, n, dtype = P, P, 128, 10, BF16
+    stride = [4 * 10 * 128, 10 * 128, 128]
+    if case == "null_x":
+        x = None
+    elif case == "null_codes":
+        codes = None
+    elif case == "d_not_multiple":
+        d = 48
+    elif case == "d_zero":
+        d = 0
+    elif case == "negative_n":
+        n = -1
+    elif case == "f32":
+        dtype = FP32
+    elif case == "misaligned_x":
+        x = P + 2
+    elif case == "misaligned_codes":
+        codes = P + 8
+    elif case == "misaligned_stride":
+        stride[2] = 132
+    st = lib.blasst_quantize_mxfp4(x, (ctypes.c_int64 * 3)(*stride), 1, 4, n, d, dtype, codes, P,
+                                   None)
+    assert st == expect, _err()
+    assert _err() != ""
 
 
 @pytest.mark.parametrize("case,expect", [

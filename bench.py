@@ -30,6 +30,11 @@ inputs already resident in HBM. The line printed on stdout carries:
   prefill_backward
                dq, dk, dv of the same layer with the forward's mask held fixed:
                algorithmic TFLOP/s (5 products per kept tile) against the peak
+  prefill_twopass
+               the two-pass variant on the same layer (MXFP4 max pre-pass, then
+               exact attention over the kept tiles): time against the one-pass
+               call, the pre-pass share, agreement of its map with the exact
+               rule's mask, and FP4 TFLOP/s of the pre-pass
   decode       the batch-32 GQA decode over 65536 keys and the batch-16 MLA
                decode over 32768 latent keys: GB/s of the bytes actually read
                (K always, V only for tiles some head keeps) against 8 TB/s
@@ -51,6 +56,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP4_TFLOPS = 10100.0  # MI355X dense FP4 MFMA
 PEAK_HBM_GBS = 8000.0
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 PREFILL_SOURCES = ["block_sparse_long_skip_amd/csrc/prefill_bf16.hip",
@@ -80,8 +86,9 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-masked", action="store_true", help="skip the block-sparse prefill leg")
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward leg")
+    ap.add_argument("--no-twopass", action="store_true", help="skip the two-pass prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
-    ap.add_argument("--only", choices=["prefill", "prefill_masked", "backward", "decode_gqa",
+    ap.add_argument("--only", choices=["prefill", "prefill_masked", "backward", "twopass", "decode_gqa",
                                        "decode_mla", "copy"],
                     help="launch only this kernel --steps times (for rocprofv3 counter passes)")
     return ap.parse_args()
@@ -227,6 +234,58 @@ def bench_prefill_masked(args, dense_ms):
                 log(f"[bench]   masked gain {gain} density {density} lam {lam}: {ms:.3f} ms "
                     f"{tf:.0f} TFLOP/s, visited {int(visited)} kept {int(kept)}")
             del bm
+        del q, k, v
+        torch.cuda.empty_cache()
+    return rows
+
+
+def bench_twopass(args):
+    """Two-pass prefill on the bench layer (MXFP4 max pre-pass, then exact
+    attention over the kept tiles) against the one-pass call at the same lambda.
+    Pass 2 is timed alone as the block-sparse call over the map at lambda 0; the
+    rest of the call (MXFP4 quantization of q and k and the map kernel) is the
+    pre-pass, priced at 2 Br Bc d FP4 FLOPs per visited tile against the FP4 peak."""
+    import torch
+    from block_sparse_long_skip_amd import attention as A
+    from block_sparse_long_skip_amd import synth
+
+    w = synth.WORKLOADS[2]
+    ws = torch.empty(A.prefill_twopass_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk),
+                     dtype=torch.uint8, device="cuda")
+    rows = []
+    for gain, lams in ((1.0, (args.lam,)), (6.0, (1e-3, 1e-2, 1e-1))):
+        log(f"[bench] generating {w.name} gain {gain} for the two-pass prefill")
+        inp = synth.make_inputs(w.with_gain(gain))
+        q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+        del inp
+        for lam in lams:
+            steps, warm = max(3, args.steps // 2), max(args.warmup, 5)
+            one_ms, _, one = time_calls(lambda: A.prefill(q, k, v, lam, causal=True), steps, warm)
+            two_ms, _, two = time_calls(lambda: A.prefill_twopass(q, k, v, lam, causal=True,
+                                                                  workspace=ws), steps, warm)
+            kept = two.mask == 1
+            p2_ms, _, _ = time_calls(lambda: A.prefill_masked(q, k, v, kept, 0.0, causal=True,
+                                                              want_mask=False, want_stats=False),
+                                     steps, warm)
+            pre_ms = max(two_ms - p2_ms, 1e-6)
+            visited = (two.mask != 2)
+            n_vis = int(visited.sum().item())
+            agree = int(((two.mask == one.mask) & visited).sum().item())
+            fp4_tf = 2.0 * w.br * w.bc * w.d * n_vis / (pre_ms * 1e-3) / 1e12
+            dev = (two.out.float() - one.out.float()).abs().max().item()
+            rows.append(dict(gain=gain, lam=lam, ms=round(two_ms, 4), one_pass_ms=round(one_ms, 4),
+                             speedup_vs_one_pass=round(one_ms / two_ms, 3),
+                             prepass_ms=round(pre_ms, 4), pass2_ms=round(p2_ms, 4),
+                             skip_fraction=round(two.skip_fraction, 4),
+                             one_pass_skip_fraction=round(one.skip_fraction, 4),
+                             map_agreement=round(agree / max(n_vis, 1), 5),
+                             max_abs_out_vs_one_pass=round(dev, 5),
+                             prepass_fp4_tflops=round(fp4_tf, 1),
+                             prepass_frac_fp4=round(fp4_tf / PEAK_FP4_TFLOPS, 4)))
+            log(f"[bench]   twopass gain {gain} lam {lam}: {two_ms:.3f} ms (pre {pre_ms:.3f} + "
+                f"pass2 {p2_ms:.3f}) vs one-pass {one_ms:.3f} ms; skip {two.skip_fraction:.3f} "
+                f"(one-pass {one.skip_fraction:.3f}), map agreement {agree / max(n_vis, 1):.4f}")
+            del one, two, kept, visited
         del q, k, v
         torch.cuda.empty_cache()
     return rows
@@ -386,6 +445,16 @@ def only(args):
         torch.cuda.synchronize()
         log(f"[bench] copied {n} bytes x {args.steps}")
         return
+    if args.only == "twopass":
+        w = synth.WORKLOADS[2]
+        inp = synth.make_inputs(w.with_gain(6.0))
+        q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+        del inp
+        for _ in range(args.steps):
+            A.prefill_twopass(q, k, v, 1e-2, causal=True)
+        torch.cuda.synchronize()
+        log(f"[bench] launched two-pass x {args.steps}")
+        return
     if args.only == "backward":
         w = synth.WORKLOADS[2]
         q, k, v, fwd, dout = backward_inputs(w, args.lam, 1.0)
@@ -435,6 +504,7 @@ def main():
     dense_ms = next((x["ms"] for x in pre["sweep"] if x["gain"] == 1.0 and x["lam"] == 0.0), None)
     masked = None if args.no_masked or dense_ms is None else bench_prefill_masked(args, dense_ms)
     backward = None if args.no_backward else bench_backward(args)
+    twopass = None if args.no_twopass else bench_twopass(args)
     decode = None if args.no_decode else bench_decode(args)
     cpu = None if args.no_cpu_baseline else cpu_baseline(args, w)
     line = {
@@ -458,6 +528,7 @@ def main():
         "lambda_sweep": pre["sweep"],
         "block_sparse_prefill": masked,
         "prefill_backward": backward,
+        "prefill_twopass": twopass,
         "decode": decode,
         "wall_s": round(time.perf_counter() - t_start, 1),
     }

@@ -36,6 +36,7 @@ constexpr int NT = 256;
 constexpr int BR = 128;  // query tile
 constexpr int BC = 64;   // key tile
 constexpr int ROWB = 64; // code bytes per row (d = 128)
+constexpr int TPS = 4;   // key tiles per LDS stage of the map kernel
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 
 // E2M1 code (magnitude index 0..7) of a >= 0: nearest of 0, .5, 1, 1.5, 2, 3,
@@ -54,6 +55,9 @@ __device__ __forceinline__ int floor_log2(float a) {
   const int ef = (int)(bits >> 23);
   return ef != 0 ? ef - 127 : (31 - __clz((int)bits)) - 149;
 }
+
+// chunk swizzle of key row r in the LDS stage
+__device__ __forceinline__ int swz_k(int r) { return (r >> 1) & 3; }
 
 __device__ __forceinline__ i32x8_t operand(const u32x4_t& v) {
   return (i32x8_t){(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
@@ -107,6 +111,12 @@ __global__ void __launch_bounds__(NT) mx_quantize_fp4_kernel(MxQuantArgs a) {
 }
 
 __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
+  // K codes and scales of TPS consecutive key tiles per stage, two stages.
+  // Codes of key r (64 bytes, four 16-byte chunks) sit at r * 64 with chunk c
+  // stored at position c ^ swz(r), so the 16-byte operand reads of 8
+  // consecutive keys fall in distinct banks.
+  __shared__ __attribute__((aligned(16))) char kbuf[2][TPS][BC * ROWB];
+  __shared__ __attribute__((aligned(16))) uint32_t sbuf[2][TPS][BC];
   __shared__ uint8_t flag[kPrefillMaxSetTiles];
 
   const int t = threadIdx.x;
@@ -130,6 +140,7 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
   const int last_row = min(i * BR + BR - 1, a.Nq - 1);
   const int first_pos = i * BR + (a.Nk - a.Nq);
   const int J = a.causal ? min(a.nkt, (last_row + a.Nk - a.Nq) / BC + 1) : a.nkt;
+  const int nstage = (J + TPS - 1) / TPS;
 
   for (int x = t; x < J; x += NT) flag[x] = 0;
 
@@ -147,40 +158,60 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
   const uint8_t* kc = a.kc + kbase * ROWB;
   const uint8_t* ks = a.ks + kbase * 4;
 
-  // K rows of tile j as A operands: key half kb, lane (key 32kb + l32, h);
-  // rows past Nk read the last key and are masked below
-  struct Tile {
-    u32x4_t c[2][2];
-    uint32_t s[2];
-  };
-  auto load_tile = [&](int j, Tile& T) __attribute__((always_inline)) {
+  // Copies of stage st into buffer st & 1: wave w moves the codes of keys
+  // 16w .. 16w + 15 of each tile (lane -> key 16w + lane / 4, physical chunk
+  // lane % 4, fetching the logical chunk stored there); wave (tile % 4) moves
+  // that tile's 64 scale words. Keys past Nk repeat the last key.
+  const int ckey = 16 * w + (lane >> 2);
+  const int cchunk = (lane & 3) ^ swz_k(ckey);
+  auto issue = [&](int st) __attribute__((always_inline)) {
+    const int buf = st & 1;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = min(j * BC + 32 * kb + l32, a.Nk - 1);
-      T.c[kb][0] = load16(kc + (int64_t)key * ROWB + 16 * h);
-      T.c[kb][1] = load16(kc + (int64_t)key * ROWB + 32 + 16 * h);
-      T.s[kb] = *(const uint32_t*)(ks + (int64_t)key * 4);
+    for (int u = 0; u < TPS; ++u) {
+      const int j = st * TPS + u;
+      if (j < J) {
+        const int key = min(j * BC + ckey, a.Nk - 1);
+        lds_dma16(kc + (int64_t)key * ROWB + 16 * cchunk, &kbuf[buf][u][w * 1024]);
+        if (w == (u & 3)) {
+          const int skey = min(j * BC + lane, a.Nk - 1);
+          __builtin_amdgcn_global_load_lds(ks + (int64_t)skey * 4,
+                                           (__attribute__((address_space(3))) void*)&sbuf[buf][u][0],
+                                           4, 0, 0);
+        }
+      }
     }
   };
 
-  __syncthreads();  // flags cleared
+  // operand reads of key half kb: key 32kb + l32, logical chunks h and 2 + h
+  int aoff[2][2];
+#pragma unroll
+  for (int kb = 0; kb < 2; ++kb) {
+    const int key = 32 * kb + l32;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) aoff[kb][kk] = key * ROWB + 16 * ((2 * kk + h) ^ swz_k(key));
+  }
 
-  float m = kNegInf;  // prefix max of this row's tile maxima (raw q.k units)
-  Tile cur, nxt;
-  load_tile(0, cur);
-  for (int j = 0; j < J; ++j) {
-    if (j + 1 < J) load_tile(j + 1, nxt);
-    f32x16_t s[2];
+  // S^T of tile u of the stage in buffer buf: keys 32kb + 8(r/4) + 4h + r%4
+  // of the tile in register r of s[kb], this lane's row in its column
+  auto scores = [&](int buf, int u, f32x16_t (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int ks0 = (int)((cur.s[kb] >> (8 * h)) & 0xffu);
-      const int ks1 = (int)((cur.s[kb] >> (16 + 8 * h)) & 0xffu);
+      const uint32_t sw = sbuf[buf][u][32 * kb + l32];
+      const int ks0 = (int)((sw >> (8 * h)) & 0xffu);
+      const int ks1 = (int)((sw >> (16 + 8 * h)) & 0xffu);
+      const u32x4_t k0 = *(const u32x4_t*)&kbuf[buf][u][aoff[kb][0]];
+      const u32x4_t k1 = *(const u32x4_t*)&kbuf[buf][u][aoff[kb][1]];
       f32x16_t acc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      acc = mfma_fp4(operand(cur.c[kb][0]), ks0, qb0, qs0, acc);
-      s[kb] = mfma_fp4(operand(cur.c[kb][1]), ks1, qb1, qs1, acc);
+      acc = mfma_fp4(operand(k0), ks0, qb0, qs0, acc);
+      s[kb] = mfma_fp4(operand(k1), ks1, qb1, qs1, acc);
     }
+  };
+
+  float m = kNegInf;  // prefix max of this row's tile maxima (raw q.k units)
+  // tile j: row max over visible keys, the row's vote, the workgroup flag
+  auto decide = [&](int j, f32x16_t (&s)[2]) __attribute__((always_inline)) {
     const int c0 = j * BC;
     if (c0 + BC > a.Nk || (a.causal && c0 + BC - 1 > first_pos)) {
 #pragma unroll
@@ -191,18 +222,38 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
           if (col >= a.Nk || (a.causal && col > qpos)) s[kb][r] = kNegInf;
         }
     }
-    float mt = fmaxf(s[0][0], s[1][0]);
+    float mt = kNegInf;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mt = fmaxf(mt, fmaxf(s[0][r], s[1][r]));
+    for (int r = 0; r < 16; ++r) mt = fmaxf(fmaxf(mt, s[0][r]), s[1][r]);
     mt = max_with_lane_xor32(mt);
-    float gap;
-    if (mt == kNegInf) gap = kNegInf;
-    else if (m == kNegInf) gap = __builtin_inff();
-    else gap = mt - m;
+    // keep unless the gap is below the threshold; a row with no visible key
+    // has gap -inf, and a row with no running max yet has gap +inf (mt - m
+    // is +inf when m = -inf and mt is finite; no NaN can arise)
+    const float gap = mt == kNegInf ? kNegInf : mt - m;
     const bool keep = valid && !(gap < a.thr_raw);
     if (__ballot(keep) != 0ull && lane == 0) flag[j] = 1;
     m = fmaxf(m, mt);
-    if (j + 1 < J) cur = nxt;
+  };
+
+  issue(0);
+  for (int st = 0; st < nstage; ++st) {
+    wait_vmem();
+    __syncthreads();  // stage st landed; every wave is done with stage st - 1
+    if (st + 1 < nstage) issue(st + 1);
+    const int buf = st & 1;
+    const int j0 = st * TPS;
+    // the next tile's MFMAs are issued before this tile's reduction
+    f32x16_t sa[2], sb[2];
+    scores(buf, 0, sa);
+#pragma unroll
+    for (int u = 0; u < TPS; u += 2) {
+      if (j0 + u >= J) break;
+      if (j0 + u + 1 < J) scores(buf, u + 1, sb);
+      decide(j0 + u, sa);
+      if (j0 + u + 1 >= J) break;
+      if (u + 2 < TPS && j0 + u + 2 < J) scores(buf, u + 2, sa);
+      decide(j0 + u + 1, sb);
+    }
   }
   __syncthreads();
 

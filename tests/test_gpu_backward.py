@@ -168,3 +168,25 @@ def test_prefill_backward_llama8b_n32768(lam, gain):
                                                    128, 64, magnitudes=True)
     _check("dk suffix", dk[:, :1, r0:], rk[:, :, r0:], mk[:, :, r0:], f"lam={lam} g={gain}")
     _check("dv suffix", dv[:, :1, r0:], rv[:, :, r0:], mv[:, :, r0:], f"lam={lam} g={gain}")
+
+
+def test_prefill_backward_strided_layout_matches_contiguous():
+    """[B, N, H, d] storage of q, k, v, out and dout gives the same gradient bits
+    as [B, H, N, d] (a layout property of the GPU path; the forward's mask, lse
+    and out feed both calls)."""
+    w = synth.small_workload("prefill", B=2, Hq=4, Hkv=2, Nq=257, Nk=400, d=128, dtype="bf16",
+                             br=128, bc=64, gain=6.0, seed=57, window=32, causal=True)
+    inp = synth.make_inputs(w)
+    q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    fwd = A.prefill(q, k, v, 1e-2)
+    g = torch.from_numpy(_dout(np.random.default_rng(8), (w.B, w.Hq, w.Nq, w.dv))).view(
+        torch.bfloat16).cuda()
+    ref = A.prefill_backward(q, k, v, fwd.out, g, fwd.lse, fwd.mask)
+    il = lambda x: x.transpose(1, 2).contiguous().transpose(1, 2)
+    qs, ks, vs, os_, gs = (il(x) for x in (q, k, v, fwd.out, g))
+    assert qs.stride(2) == w.Hq * w.d and os_.stride() == gs.stride()
+    got = A.prefill_backward(qs, ks, vs, os_, gs, fwd.lse, fwd.mask)
+    torch.cuda.synchronize()
+    assert got[0].stride() == qs.stride() and got[1].stride() == ks.stride()
+    for r, x in zip(ref, got):
+        assert torch.equal(r, x)

@@ -217,3 +217,51 @@ def test_prefill_twopass_llama8b_n32768(lam, gain, out):
     tally.check(w.dtype, f"twopass llama8b lam={lam} g={gain}", out_bf16=out == "bf16")
     if gain > 1.0:
         assert res.skip_fraction > 0.05
+
+
+def test_prefill_twopass_map_in_workspace_matches():
+    """Without mask_out the map lives in the workspace; out, lse and statistics
+    are the same bits as with it."""
+    w = synth.small_workload("prefill", B=2, Hq=4, Hkv=2, Nq=300, Nk=700, d=128, dtype="bf16",
+                             br=128, bc=64, gain=6.0, seed=64, window=32, causal=True)
+    inp = synth.make_inputs(w)
+    q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    ref = A.prefill_twopass(q, k, v, 1e-2, causal=True)
+    got = A.prefill_twopass(q, k, v, 1e-2, causal=True, want_mask=False)
+    torch.cuda.synchronize()
+    assert got.mask is None
+    assert torch.equal(ref.out.view(torch.int16), got.out.view(torch.int16))
+    assert torch.equal(ref.lse, got.lse)
+    assert torch.equal(ref.stats, got.stats)
+
+
+def test_prefill_twopass_strided_layout_matches_contiguous():
+    """[B, N, H, d] storage (heads interleaved) gives the same bits as [B, H, N, d]."""
+    w = synth.small_workload("prefill", B=2, Hq=4, Hkv=2, Nq=257, Nk=400, d=128, dtype="bf16",
+                             br=128, bc=64, gain=6.0, seed=65, window=32, causal=True)
+    inp = synth.make_inputs(w)
+    q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    ref = A.prefill_twopass(q, k, v, 1e-2, causal=True)
+    qs, ks, vs = (x.transpose(1, 2).contiguous().transpose(1, 2) for x in (q, k, v))
+    assert qs.stride(2) == w.Hq * w.d
+    got = A.prefill_twopass(qs, ks, vs, 1e-2, causal=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ref.out.view(torch.int16), got.out.view(torch.int16))
+    assert torch.equal(ref.mask, got.mask)
+    assert torch.equal(ref.stats, got.stats)
+
+
+def test_prefill_twopass_rejected_call_leaves_outputs_untouched():
+    w = synth.small_workload("prefill", Nq=200, Nk=200, seed=66)
+    inp = synth.make_inputs(w)
+    q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    out = torch.full((1, w.Hq, 200, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(A.BlasstError) as e:
+        A.prefill_twopass(q, k, v, 1.5, out=out)
+    assert e.value.status == 4
+    small = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(A.BlasstError) as e:
+        A.prefill_twopass(q, k, v, 1e-2, out=out, workspace=small)
+    assert e.value.status == 9
+    torch.cuda.synchronize()
+    assert (out == 7.0).all()

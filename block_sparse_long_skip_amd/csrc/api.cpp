@@ -49,6 +49,12 @@ blasst_status_t ok() {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+// A tensor pointer may be NULL exactly when the tensor has no elements.
+bool missing(const void* p, int64_t elements) { return p == nullptr && elements > 0; }
+int64_t count(int64_t a, int64_t b, int64_t c) {
+  return (a > 0 && b > 0 && c > 0) ? a * b * c : 0;
+}
+
 bool strides_aligned(const int64_t* s, int n, int elem) {
   for (int i = 0; i < n; ++i)
     if (((s[i] * elem) & 15) != 0) return false;
@@ -91,9 +97,9 @@ blasst_status_t zero_stats(int64_t* stats, int64_t n, hipStream_t st) {
   return BLASST_OK;
 }
 
-// Both prefill entry points; block_mask is NULL for plain prefill.
+// Both prefill entry points (masked: block-sparse mode with block_mask).
 // Validates a prefill call and fills its kernel arguments; launches nothing.
-blasst_status_t prepare_prefill(const void* q, const void* k, const void* v,
+blasst_status_t prepare_prefill(const void* q, const void* k, const void* v, bool masked,
                                 const uint8_t* block_mask, const int64_t* block_mask_stride,
                                 void* out, uint8_t* mask_out, float* lse_out, int64_t* stats_out,
                                 const blasst_shape_t* shape, blasst_dtype_t dtype,
@@ -101,7 +107,14 @@ blasst_status_t prepare_prefill(const void* q, const void* k, const void* v,
                                 int br, int bc, blasst::PrefillArgs* args, bool* use_f32) {
   blasst_status_t st0;
   if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
-  if (!q || !k || !v || !out) return fail(BLASST_E_NULL, "q, k, v and out are required");
+  {
+    const blasst_shape_t& z = *shape;
+    const int64_t nq_el = count(z.batch, z.heads_q, z.len_q), nk_el = count(z.batch, z.heads_kv, z.len_kv);
+    if (missing(q, nq_el) || missing(out, nq_el) || missing(k, nk_el) || missing(v, nk_el))
+      return fail(BLASST_E_NULL, "q, k, v and out are required");
+    if (masked && (!block_mask_stride || missing(block_mask, nq_el)))
+      return fail(BLASST_E_NULL, "block_mask and block_mask_stride are required");
+  }
   st0 = check_dtypes(dtype, out_dtype);
   if (st0 != BLASST_OK) return st0;
   const blasst_shape_t& s = *shape;
@@ -141,7 +154,7 @@ blasst_status_t prepare_prefill(const void* q, const void* k, const void* v,
   const int64_t nkt = ((int64_t)s.len_kv + bc - 1) / bc;
   if ((int64_t)s.batch * s.heads_q * nqt > 0x7fffffffLL)
     return fail(BLASST_E_UNSUPPORTED, "grid too large");
-  if (block_mask) {
+  if (masked) {
     if (!b16)
       return fail(BLASST_E_UNSUPPORTED, "block-sparse prefill needs bf16 inputs, d = 128, 128x64 tiles");
     if (block_mask_stride[0] < 0 || block_mask_stride[1] < 0 || block_mask_stride[2] < 0)
@@ -156,9 +169,9 @@ blasst_status_t prepare_prefill(const void* q, const void* k, const void* v,
   a.q = q; a.k = k; a.v = v; a.out = out;
   a.mask = mask_out; a.lse = lse_out; a.stats = stats_out;
   a.block_mask = block_mask;
-  a.bms0 = block_mask ? block_mask_stride[0] : 0;
-  a.bms1 = block_mask ? block_mask_stride[1] : 0;
-  a.bms2 = block_mask ? block_mask_stride[2] : 0;
+  a.bms0 = masked ? block_mask_stride[0] : 0;
+  a.bms1 = masked ? block_mask_stride[1] : 0;
+  a.bms2 = masked ? block_mask_stride[2] : 0;
   a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nq = s.len_q; a.Nk = s.len_kv;
   a.nqt = (int)nqt; a.nkt = (int)nkt; a.causal = causal ? 1 : 0;
   a.out_f32 = out_dtype == BLASST_FP32 ? 1 : 0;
@@ -174,7 +187,7 @@ blasst_status_t prepare_prefill(const void* q, const void* k, const void* v,
   return BLASST_OK;
 }
 
-blasst_status_t run_prefill(const void* q, const void* k, const void* v,
+blasst_status_t run_prefill(const void* q, const void* k, const void* v, bool masked,
                             const uint8_t* block_mask, const int64_t* block_mask_stride,
                             void* out, uint8_t* mask_out, float* lse_out, int64_t* stats_out,
                             const blasst_shape_t* shape, blasst_dtype_t dtype,
@@ -182,7 +195,7 @@ blasst_status_t run_prefill(const void* q, const void* k, const void* v,
                             int br, int bc, void* stream) {
   blasst::PrefillArgs a;
   bool f32 = false;
-  blasst_status_t st = prepare_prefill(q, k, v, block_mask, block_mask_stride, out, mask_out,
+  blasst_status_t st = prepare_prefill(q, k, v, masked, block_mask, block_mask_stride, out, mask_out,
                                        lse_out, stats_out, shape, dtype, out_dtype, lambda, scale,
                                        causal, br, bc, &a, &f32);
   if (st != BLASST_OK) return st;
@@ -224,7 +237,7 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
                                     const blasst_shape_t* shape, blasst_dtype_t dtype,
                                     blasst_dtype_t out_dtype, float lambda, float scale,
                                     int causal, int br, int bc, void* stream) {
-  return run_prefill(q, k, v, nullptr, nullptr, out, mask_out, lse_out, stats_out, shape, dtype,
+  return run_prefill(q, k, v, false, nullptr, nullptr, out, mask_out, lse_out, stats_out, shape, dtype,
                      out_dtype, lambda, scale, causal, br, bc, stream);
 }
 
@@ -236,9 +249,7 @@ blasst_status_t blasst_attn_prefill_masked(const void* q, const void* k, const v
                                            blasst_dtype_t dtype, blasst_dtype_t out_dtype,
                                            float lambda, float scale, int causal, int br, int bc,
                                            void* stream) {
-  if (!block_mask || !block_mask_stride)
-    return fail(BLASST_E_NULL, "block_mask and block_mask_stride are required");
-  return run_prefill(q, k, v, block_mask, block_mask_stride, out, mask_out, lse_out, stats_out,
+  return run_prefill(q, k, v, true, block_mask, block_mask_stride, out, mask_out, lse_out, stats_out,
                      shape, dtype, out_dtype, lambda, scale, causal, br, bc, stream);
 }
 
@@ -304,7 +315,10 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
                                    float scale, int bc, void* workspace, size_t workspace_bytes,
                                    void* stream) {
   if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
-  if (!q || !k_cache || !out) return fail(BLASST_E_NULL, "q, k_cache and out are required");
+  if (missing(q, count(shape->batch, shape->heads_q, 1)) ||
+      missing(out, count(shape->batch, shape->heads_q, 1)) ||
+      missing(k_cache, count(shape->batch, shape->heads_kv, shape->len_kv)))
+    return fail(BLASST_E_NULL, "q, k_cache and out are required");
   blasst_status_t st = check_dtypes(dtype, out_dtype);
   if (st != BLASST_OK) return st;
   const blasst_shape_t& s = *shape;
@@ -425,8 +439,14 @@ blasst_status_t blasst_attn_prefill_backward(
     const blasst_shape_t* shape, blasst_dtype_t dtype, blasst_dtype_t out_dtype, float scale,
     int causal, int br, int bc, void* workspace, size_t workspace_bytes, void* stream) {
   if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
-  if (!q || !k || !v || !out || !dout || !lse || !mask || !dq || !dk || !dv)
-    return fail(BLASST_E_NULL, "q, k, v, out, dout, lse, mask, dq, dk and dv are required");
+  {
+    const int64_t nq_el = count(shape->batch, shape->heads_q, shape->len_q);
+    const int64_t nk_el = count(shape->batch, shape->heads_kv, shape->len_kv);
+    if (missing(q, nq_el) || missing(out, nq_el) || missing(dout, nq_el) || missing(lse, nq_el) ||
+        missing(mask, nq_el) || missing(dq, nq_el) || missing(k, nk_el) || missing(v, nk_el) ||
+        missing(dk, nk_el) || missing(dv, nk_el))
+      return fail(BLASST_E_NULL, "q, k, v, out, dout, lse, mask, dq, dk and dv are required");
+  }
   const blasst_shape_t& s = *shape;
   blasst_status_t st = check_backward(s, dtype, causal, br, bc);
   if (st != BLASST_OK) return st;
@@ -539,7 +559,8 @@ extern "C" {
 blasst_status_t blasst_quantize_mxfp4(const void* x, const int64_t x_stride[3], int32_t d0,
                                       int32_t d1, int32_t n, int32_t d, blasst_dtype_t dtype,
                                       uint8_t* codes, uint8_t* scales, void* stream) {
-  if (!x || !x_stride || !codes || !scales)
+  const int64_t nrows = count(d0, d1, n);
+  if (!x_stride || missing(x, nrows) || missing(codes, nrows) || missing(scales, nrows))
     return fail(BLASST_E_NULL, "x, x_stride, codes and scales are required");
   if (d0 < 0 || d1 < 0 || n < 0 || d < 32 || d % 32 != 0)
     return fail(BLASST_E_SHAPE, "need d0, d1, n >= 0 and d a positive multiple of 32 (got %d %d %d %d)",
@@ -577,6 +598,8 @@ blasst_status_t blasst_attn_prefill_twopass(const void* q, const void* k, const 
   blasst_status_t st = check_twopass(s, dtype, causal, br, bc);
   if (st != BLASST_OK) return st;
   const TwoPassLayout L = twopass_layout(s, br, bc);
+  st = check_workspace(workspace, workspace_bytes, L.total);
+  if (st != BLASST_OK) return st;
   // the second pass is the block-sparse prefill over the map; validating it
   // first covers every pointer, stride and size rule of the inputs and outputs
   char* ws = static_cast<char*>(workspace);
@@ -585,11 +608,8 @@ blasst_status_t blasst_attn_prefill_twopass(const void* q, const void* k, const 
   const int64_t map_stride[3] = {(int64_t)s.heads_q * nqt * nkt, (int64_t)nqt * nkt, nkt};
   blasst::PrefillArgs a2;
   bool f32 = false;
-  st = prepare_prefill(q, k, v, map, map_stride, out,
-                       nullptr, lse_out, nullptr, shape, dtype, out_dtype, lambda, scale, causal,
-                       br, bc, &a2, &f32);
-  if (st != BLASST_OK) return st;
-  st = check_workspace(workspace, workspace_bytes, L.total);
+  st = prepare_prefill(q, k, v, true, map, map_stride, out, nullptr, lse_out, nullptr, shape,
+                       dtype, out_dtype, lambda, scale, causal, br, bc, &a2, &f32);
   if (st != BLASST_OK) return st;
   a2.thr_raw = raw_threshold(0.f, a2.scale);  // exact softmax over the kept tiles
 

@@ -43,6 +43,11 @@
  *   - Tensor pointers must be 16-byte aligned, the last dimension must be
  *     contiguous, and every stride times the element size must be a multiple
  *     of 16 bytes (BLASST_E_ALIGN).
+ *   - A tensor pointer may be NULL exactly when its tensor has no elements
+ *     (batch = 0, or len_q = 0 for the query-side tensors); otherwise a NULL
+ *     required pointer is BLASST_E_NULL. A call with no query rows launches
+ *     only what fills its non-empty outputs: statistics are zeroed, and the
+ *     backward writes zero dk and dv.
  *   - lambda must satisfy 0 <= lambda <= 1 (BLASST_E_LAMBDA otherwise; NaN is
  *     rejected). lambda = 0 drops nothing and gives exact softmax attention.
  *   - scale <= 0 selects 1/sqrt(d_qk); a non-finite scale is BLASST_E_ARG.
@@ -159,7 +164,8 @@ blasst_status_t blasst_attn_prefill(const void* q, const void* k, const void* v,
  *
  * Supported (else BLASST_E_UNSUPPORTED): BLASST_BF16, d_qk = d_v = 128,
  * br = 128, bc = 64, ceil(Nk/64) <= 6144 (Nk <= 393216).
- * NULL block_mask or block_mask_stride is BLASST_E_NULL; a negative stride is
+ * NULL block_mask_stride, or NULL block_mask for a call with query rows, is
+ * BLASST_E_NULL; a negative stride is
  * BLASST_E_SHAPE.
  */
 blasst_status_t blasst_attn_prefill_masked(const void* q, const void* k, const void* v,

@@ -399,3 +399,41 @@ def test_binding_has_no_cpu_fallback():
     q = torch.zeros(1, 1, 64, 64)
     with pytest.raises(Exception):
         A.prefill(q, q, q, 0.0)
+
+
+def test_empty_calls_accept_null_tensors():
+    """A tensor pointer may be NULL when the tensor has no elements; such calls
+    succeed (no query rows and no statistics: nothing to launch)."""
+    lib = A.load_library()
+    sh = _shape(B=0)
+    assert lib.blasst_attn_prefill(None, None, None, None, None, None, None, ctypes.byref(sh), BF16,
+                                   BF16, 1e-3, 0.0, 1, 128, 64, None) == 0, _err()
+    bms = (ctypes.c_int64 * 3)(0, 0, 0)
+    assert lib.blasst_attn_prefill_masked(None, None, None, None, bms, None, None, None, None,
+                                          ctypes.byref(sh), BF16, BF16, 1e-3, 0.0, 1, 128, 64,
+                                          None) == 0, _err()
+    assert lib.blasst_attn_prefill_twopass(None, None, None, None, None, None, None, ctypes.byref(sh),
+                                           BF16, BF16, 1e-3, 0.0, 1, 128, 64, None, 0, None) == 0, _err()
+    assert lib.blasst_attn_prefill_backward(None, None, None, None, None, None, None, None, None, None,
+                                            ctypes.byref(sh), BF16, BF16, 0.0, 1, 128, 64, None, 0,
+                                            None) == 0, _err()
+    # decode: a NULL v_cache selects the latent layout, so an empty GQA call
+    # passes some V pointer and an empty latent call passes none
+    shd = _shape(B=0, Hq=8, Hkv=2, Nq=1, Nk=1000)
+    assert lib.blasst_attn_decode(None, None, P, None, None, None, None, ctypes.byref(shd), BF16,
+                                  BF16, 1e-3, 0.0, 64, None, 0, None) == 0, _err()
+    shl = _shape(B=0, Hq=128, Hkv=1, Nq=1, Nk=1000, d=576, dv=512)
+    assert lib.blasst_attn_decode(None, None, None, None, None, None, None, ctypes.byref(shl), BF16,
+                                  BF16, 1e-3, 0.0, 64, None, 0, None) == 0, _err()
+    assert lib.blasst_quantize_mxfp4(None, (ctypes.c_int64 * 3)(0, 0, 128), 1, 4, 0, 128, BF16, None,
+                                     None, None) == 0, _err()
+    # no query rows but a key range: q and out may be NULL, k and v may not
+    sh = _shape(Nq=0)
+    assert lib.blasst_attn_prefill(None, P, P, None, None, None, None, ctypes.byref(sh), BF16, BF16,
+                                   1e-3, 0.0, 1, 128, 64, None) == 0, _err()
+    assert lib.blasst_attn_prefill(None, None, P, None, None, None, None, ctypes.byref(sh), BF16,
+                                   BF16, 1e-3, 0.0, 1, 128, 64, None) == 1
+    # a block-sparse call still needs its strides
+    assert lib.blasst_attn_prefill_masked(None, P, P, None, None, None, None, None, None,
+                                          ctypes.byref(sh), BF16, BF16, 1e-3, 0.0, 1, 128, 64,
+                                          None) == 1

@@ -100,6 +100,10 @@ def test_prefill_fp32_ragged(shape, lam, gain):
     dict(B=1, Hq=1, Hkv=1, Nq=128, Nk=128, causal=True),
     dict(B=1, Hq=1, Hkv=1, Nq=5, Nk=64, causal=True),
     dict(B=1, Hq=1, Hkv=1, Nq=1, Nk=1, causal=True),
+    # several query tiles with ragged key ranges (bottom-right causal) and a
+    # non-causal shape with drops in every query tile
+    dict(B=1, Hq=2, Hkv=1, Nq=384, Nk=1000, causal=True),
+    dict(B=1, Hq=1, Hkv=1, Nq=512, Nk=700, causal=False),
 ])
 @pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 1.0), (1e-2, 6.0), (1.0, 6.0)])
 @pytest.mark.parametrize("out", ["bf16", "fp32"])

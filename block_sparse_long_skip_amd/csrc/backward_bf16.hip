@@ -12,7 +12,7 @@
 // dK and dV of a KV head summed over the query heads that read it. P is
 // recomputed from the forward's lse; only kept tiles are visited.
 //
-// Three kernels:
+// Kernels:
 //   bwd_delta_kernel  delta[row] = dO[row] . O[row] (fp32), into the workspace.
 //   bwd_dq_kernel     one workgroup of 4 waves per (batch, query head, query
 //                     tile), wave w owning rows 32w..32w+31, laid out like the
@@ -23,17 +23,19 @@
 //                     permuted to match the accumulator layout. The kept key
 //                     tiles of the query tile are listed in LDS first; K and V
 //                     tiles are double-buffered.
-//   bwd_dkdv_kernel   one workgroup of 4 waves per (batch, KV head, key tile),
-//                     wave w = (key half kh = w & 1, row half rh = w >> 1).
-//                     S = Q K^T and dP = dO V^T put one key in each lane column
-//                     (K and V rows of the lane's key live in registers as the
-//                     B operands), so P and dS come out of the accumulators
+//   bwd_kv_kernel     dV (one launch) and dK (a second launch): one workgroup
+//                     of 4 waves per (batch, KV head, pair of key tiles), wave
+//                     w owning keys 32w..32w+31 of the pair. S = Q K^T (and for
+//                     dK, dP = dO V^T) put one key in each lane column (the K
+//                     and V rows of the lane's key live in registers as the B
+//                     operands), so P and dS come out of the accumulators
 //                     already in the A-operand layout of dV += P^T dO and
-//                     dK += dS^T Q; dO and Q are read transposed from 128-row
-//                     LDS tiles (double-buffered), rows permuted the same way.
+//                     dK += dS^T Q; dO and Q are read transposed from 64-row
+//                     LDS stages (double-buffered), rows permuted the same way.
 //                     The workgroup walks every query head of the KV group and
-//                     the query tiles whose mask byte for this key tile is 1;
-//                     the two row halves are summed through LDS at the end.
+//                     the query tiles whose mask byte for either key tile is 1.
+//                     Splitting dV from dK (S recomputed once more) keeps each
+//                     launch within two workgroups per CU.
 #include <type_traits>
 
 #include "common.hpp"
@@ -319,11 +321,21 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(BackwardArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(BackwardArgs a) {
-  __shared__ __attribute__((aligned(16))) char Qs[2][QTILE];
-  __shared__ __attribute__((aligned(16))) char Gs[2][QTILE];  // dO
-  __shared__ __attribute__((aligned(16))) float LD[2][2][BR];  // [buffer][lse, delta][row]
-  __shared__ uint16_t ilist[kBackwardMaxTiles];
+// dV (DK = false) or dK (DK = true) of two consecutive key tiles (128 keys),
+// in separate launches so that each fits two workgroups per CU. dV recomputes
+// S; dK recomputes S and dP. Wave w owns keys 32w .. 32w+31 of the pair (key
+// tile w / 2) over every query row, so each 64-row stage of Q, dO, lse and
+// delta copied into LDS (double-buffered) serves 128 keys and no partial sums
+// are exchanged. The workgroup visits the query tiles that keep either key
+// tile; a wave whose key tile a query tile drops skips it.
+template <bool DK>
+__global__ void __launch_bounds__(NT, 2) bwd_kv_kernel(BackwardArgs a) {
+  constexpr int SR = 64;             // query rows per LDS stage
+  constexpr int STILE = SR * D * 2;  // 16 KB
+  __shared__ __attribute__((aligned(16))) char Qs[2][STILE];
+  __shared__ __attribute__((aligned(16))) char Gs[2][STILE];  // dO
+  __shared__ __attribute__((aligned(16))) float LD[2][2][SR];  // [buffer][lse, delta][row]
+  __shared__ uint16_t ilist[kBackwardMaxTiles];  // (query tile << 2) | keeps of the two key tiles
   __shared__ int wcount[4];
 
   const int t = threadIdx.x;
@@ -331,43 +343,37 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(BackwardArgs a) {
   const int w = t >> 6;
   const int l32 = lane & 31;
   const int h = lane >> 5;
-  const int kh = w & 1, rh = w >> 1;
+  const int kt = w >> 1, kh = w & 1;  // key tile of the pair, key half
 
-  // block -> (key tile, (batch, KV head)): low key tiles (most query tiles
-  // when causal) first
+  // block -> (key-tile pair, (batch, KV head)): low key tiles (most query
+  // tiles when causal) first
   const int nbk = a.B * a.Hkv;
-  const int j = (int)(blockIdx.x / nbk);
+  const int jp = (int)(blockIdx.x / nbk);
   const int bk = (int)(blockIdx.x % nbk);
   const int b = bk / a.Hkv, kvh = bk % a.Hkv;
   const int G = a.Hq / a.Hkv;
+  const int j = 2 * jp + kt;  // this wave's key tile
   const int c0 = j * BC;
   const int key = c0 + 32 * kh + l32;  // this lane's key (MFMA column)
   const bool kvalid = key < a.Nk;
   const float c2 = a.scale_log2;
 
-  // K and V rows of the lane's key as B operands: features 16kk + 8h .. +7
-  bf16x8_t kb[D / 16], vb[D / 16];
+  // K (and for dK, V) rows of the lane's key as B operands: features
+  // 16kk + 8h .. +7; keys past the end load the last key and are zeroed
+  bf16x8_t kb[D / 16], vb[DK ? D / 16 : 1];
   {
-    // keys past the end load the last key (no branch) and are zeroed
     const int64_t kc = min(key, a.Nk - 1);
     const uint16_t* kp = (const uint16_t*)a.k + b * a.ks0 + kvh * a.ks1 + kc * a.ks2;
     const uint16_t* vp = (const uint16_t*)a.v + b * a.vs0 + kvh * a.vs1 + kc * a.vs2;
-    u32x4_t xk[D / 16], xv[D / 16];
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      xk[kk] = load16(kp + 16 * kk + 8 * h);
-      xv[kk] = load16(vp + 16 * kk + 8 * h);
-    }
     const uint32_t keep = kvalid ? 0xffffffffu : 0u;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      kb[kk] = as_bf16x8(xk[kk] & keep);
-      vb[kk] = as_bf16x8(xv[kk] & keep);
+      kb[kk] = as_bf16x8(load16(kp + 16 * kk + 8 * h) & keep);
+      if constexpr (DK) vb[kk] = as_bf16x8(load16(vp + 16 * kk + 8 * h) & keep);
     }
   }
 
-  // A-operand reads of a 128-row tile (rows as MFMA rows): row base + l32,
-  // chunk 2kk + h
+  // A-operand reads (rows as MFMA rows): row base + l32, chunk 2kk + h
   int aro[D / 16];
 #pragma unroll
   for (int kk = 0; kk < D / 16; ++kk) aro[kk] = swz(l32, 2 * kk + h);
@@ -383,214 +389,193 @@ __global__ void __launch_bounds__(NT, 1) bwd_dkdv_kernel(BackwardArgs a) {
     tro[db][0] = swz(r0, d0 >> 3) + ((d0 & 7) << 1);
     tro[db][1] = swz(r0 + 8, d0 >> 3) + ((d0 & 7) << 1);
   }
-  // tile copies of 128 rows: wave w fills rows 32w..32w+31, instruction r
-  // (0..7) rows 32w + 4r + lane/16. Every row offset is in the per-lane offset:
-  // the hardware range check (zeros past the last row) covers only that part
+  // stage copies of 64 rows: wave w fills rows 16w..16w+15, instruction r
+  // (0..3) rows 16w + 4r + lane/16
   const int sub = lane >> 4, pch = lane & 15;
-  uint32_t qoff[8], goff[8];
+  uint32_t qoff[4], goff[4];
 #pragma unroll
-  for (int r = 0; r < 8; ++r) {
-    const int trow = 32 * w + 4 * r + sub;
+  for (int r = 0; r < 4; ++r) {
+    const int trow = 16 * w + 4 * r + sub;
     const int ch = pch ^ swz_f(trow);
     qoff[r] = (uint32_t)(((int64_t)trow * a.qs2 + ch * 8) * 2);
     goff[r] = (uint32_t)(((int64_t)trow * a.dos2 + ch * 8) * 2);
   }
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  auto qtile_to_lds = [&](char* tile, const char* base, const uint32_t (&off)[8], int64_t stride,
+  auto stage_to_lds = [&](char* tile, const char* base, const uint32_t* off, int64_t stride,
                           int r0) __attribute__((always_inline)) {
     const __amdgpu_buffer_rsrc_t rs =
-        make_rsrc(base + (int64_t)r0 * stride * 2, min(a.Nq - r0, BR), stride * 2);
+        make_rsrc(base + (int64_t)r0 * stride * 2, min(a.Nq - r0, SR), stride * 2);
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
+    for (int r = 0; r < 4; ++r)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(
-          rs, (__attribute__((address_space(3))) void*)(tile + (32 * wu + 4 * r) * 256), 16, off[r],
+          rs, (__attribute__((address_space(3))) void*)(tile + (16 * wu + 4 * r) * 256), 16, off[r],
           0, 0, 0);
   };
-  // lse and delta of 128 rows: wave 0 copies 2 x 512 bytes
-  auto rows_to_lds = [&](float (&dst)[2][BR], const float* lse_row, const float* dl_row, int r0)
+  // lse (and for dK, delta) of 64 rows: wave 0 copies 256 bytes each
+  auto rows_to_lds = [&](float (&dst)[2][SR], const float* lse_row, const float* dl_row, int r0)
       __attribute__((always_inline)) {
     if (wu == 0) {
-      const __amdgpu_buffer_rsrc_t rl = make_rsrc((const char*)(lse_row + r0), min(a.Nq - r0, BR), 4);
-      const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char*)(dl_row + r0), min(a.Nq - r0, BR), 4);
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
+      const __amdgpu_buffer_rsrc_t rl = make_rsrc((const char*)(lse_row + r0), min(a.Nq - r0, SR), 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rl, (__attribute__((address_space(3))) void*)(&dst[0][0]), 4, 4 * lane, 0, 0, 0);
+      if constexpr (DK) {
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc((const char*)(dl_row + r0), min(a.Nq - r0, SR), 4);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rl, (__attribute__((address_space(3))) void*)(&dst[0][64 * x]), 4, 4 * lane + 256 * x, 0,
-            0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rd, (__attribute__((address_space(3))) void*)(&dst[1][64 * x]), 4, 4 * lane + 256 * x, 0,
-            0, 0);
+            rd, (__attribute__((address_space(3))) void*)(&dst[1][0]), 4, 4 * lane, 0, 0, 0);
       }
     }
   };
 
-  f32x16_t dka[4], dva[4];  // dK, dV[key 8(r/4) + 4h + r%4 of the wave's 32][d = 32db + l32]
+  f32x16_t acc[4];  // dK or dV[key 8(r/4) + 4h + r%4 of the wave's 32][d = 32db + l32]
 #pragma unroll
   for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dka[db][r] = dva[db][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
 
+  const bool second = 2 * jp + 1 < a.nkt;  // the pair has a second key tile
   for (int g = 0; g < G; ++g) {
     const int hq = kvh * G + g;
     const int64_t bh = (int64_t)b * a.Hq + hq;
-    // query tiles that keep this key tile, in increasing order
-    const uint8_t* mcol = a.mask + bh * a.nqt * a.nkt + j;
+    // query tiles that keep either key tile, in increasing order
+    const uint8_t* mcol = a.mask + bh * a.nqt * a.nkt + 2 * jp;
+    auto keeps = [&](int x) __attribute__((always_inline)) -> int {
+      const uint8_t* m = mcol + (int64_t)x * a.nkt;
+      return (m[0] == 1 ? 1 : 0) | (second && m[1] == 1 ? 2 : 0);
+    };
     int n;
     {
       const int per = (a.nqt + NT - 1) / NT;
       const int x0 = min(t * per, a.nqt), x1 = min(x0 + per, a.nqt);
       int cnt = 0;
-      for (int x = x0; x < x1; ++x) cnt += mcol[(int64_t)x * a.nkt] == 1;
+      for (int x = x0; x < x1; ++x) cnt += keeps(x) != 0;
       int incl = cnt;
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) {
         const int y = __shfl_up(incl, off, 64);
         if (lane >= off) incl += y;
       }
-      __syncthreads();  // the previous head's list and tiles are no longer read
+      __syncthreads();  // the previous head's list and stages are no longer read
       if (lane == 63) wcount[w] = incl;
       __syncthreads();
       int pos = incl - cnt;
       for (int ww = 0; ww < w; ++ww) pos += wcount[ww];
       n = __builtin_amdgcn_readfirstlane(wcount[0] + wcount[1] + wcount[2] + wcount[3]);
-      for (int x = x0; x < x1; ++x)
-        if (mcol[(int64_t)x * a.nkt] == 1) ilist[pos++] = (uint16_t)x;
+      for (int x = x0; x < x1; ++x) {
+        const int kp = keeps(x);
+        if (kp) ilist[pos++] = (uint16_t)((x << 2) | kp);
+      }
       __syncthreads();
     }
     const char* qp = (const char*)((const uint16_t*)a.q + b * a.qs0 + hq * a.qs1);
     const char* gp = (const char*)((const uint16_t*)a.dout + b * a.dos0 + hq * a.dos1);
     const float* lse_row = a.lse + bh * a.Nq;
     const float* dl_row = a.delta + bh * a.Nq;
-    auto tile_at = [&](int x) __attribute__((always_inline)) -> int {
-      return __builtin_amdgcn_readfirstlane((int)ilist[x]);
+    // stage x: rows SR (x & 1) .. of the (x / 2)-th listed query tile
+    const int nst = 2 * n;
+    auto entry = [&](int x) __attribute__((always_inline)) -> int {
+      return __builtin_amdgcn_readfirstlane((int)ilist[x >> 1]);
     };
-    if (n > 0) {
-      const int r0 = tile_at(0) * BR;
-      qtile_to_lds(Qs[0], qp, qoff, a.qs2, r0);
-      qtile_to_lds(Gs[0], gp, goff, a.dos2, r0);
+    if (nst > 0) {
+      const int r0 = (entry(0) >> 2) * BR;
+      stage_to_lds(Qs[0], qp, qoff, a.qs2, r0);
+      stage_to_lds(Gs[0], gp, goff, a.dos2, r0);
       rows_to_lds(LD[0], lse_row, dl_row, r0);
     }
-    auto step = [&](auto PAR, int idx) __attribute__((always_inline)) {
+    auto step = [&](auto PAR, int x) __attribute__((always_inline)) {
       constexpr int P = decltype(PAR)::value;
       wait_vmem();
-      __syncthreads();  // query tile idx is in LDS; every wave is done with idx-1
-      if (idx + 1 < n) {
-        const int rn = tile_at(idx + 1) * BR;
-        qtile_to_lds(Qs[P ^ 1], qp, qoff, a.qs2, rn);
-        qtile_to_lds(Gs[P ^ 1], gp, goff, a.dos2, rn);
+      __syncthreads();  // stage x is in LDS; every wave is done with x-1
+      if (x + 1 < nst) {
+        const int rn = (entry(x + 1) >> 2) * BR + SR * ((x + 1) & 1);
+        stage_to_lds(Qs[P ^ 1], qp, qoff, a.qs2, rn);
+        stage_to_lds(Gs[P ^ 1], gp, goff, a.dos2, rn);
         rows_to_lds(LD[P ^ 1], lse_row, dl_row, rn);
       }
-      const int i = tile_at(idx);
-      const bool edge = (i * BR + BR > a.Nq) || (c0 + BC > a.Nk) ||
-                        (a.causal && c0 + BC - 1 > i * BR + (a.Nk - a.Nq));
+      const int e = entry(x);
+      if (!((e >> kt) & 1)) return;  // this query tile drops the wave's key tile
+      const int r0 = (e >> 2) * BR + SR * (x & 1);
+      const bool edge = (r0 + SR > a.Nq) || (c0 + BC > a.Nk) ||
+                        (a.causal && c0 + BC - 1 > r0 + (a.Nk - a.Nq));
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
-        const int rb = 64 * rh + 32 * sb;  // first row of the 32-row block in the tile
+        const int rb = 32 * sb;  // first row of the 32-row block in the stage
         const char* qt = Qs[P] + rb * 256;
         const char* gt = Gs[P] + rb * 256;
-        // S[row][key] = Q K^T and dP[row][key] = dO V^T (one chain each)
+        // S[row][key] = Q K^T (and dP[row][key] = dO V^T)
         f32x16_t s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
           const u32x4_t xq = *(const u32x4_t*)(qt + aro[kk]);
-          const u32x4_t xg = *(const u32x4_t*)(gt + aro[kk]);
           s = mfma32x32x16(as_bf16x8(xq), kb[kk], s);
-          dp = mfma32x32x16(as_bf16x8(xg), vb[kk], dp);
-        }
-        // rows of this lane's accumulators: rb + 8(r/4) + 4h + r%4
-        float l2[16], dl[16];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const f32x4_t x = *(const f32x4_t*)&LD[P][0][rb + 8 * q4 + 4 * h];
-          const f32x4_t y = *(const f32x4_t*)&LD[P][1][rb + 8 * q4 + 4 * h];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            l2[4 * q4 + e] = x[e] == kNegInf ? __builtin_inff() : x[e] * kLog2e;
-            dl[4 * q4 + e] = y[e];
+          if constexpr (DK) {
+            const u32x4_t xg = *(const u32x4_t*)(gt + aro[kk]);
+            dp = mfma32x32x16(as_bf16x8(xg), vb[kk], dp);
           }
         }
         if (edge) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int qrow = i * BR + rb + 8 * (r >> 2) + 4 * h + (r & 3);
+            const int qrow = r0 + rb + 8 * (r >> 2) + 4 * h + (r & 3);
             if (qrow >= a.Nq || !kvalid || (a.causal && key > qrow + (a.Nk - a.Nq))) s[r] = kNegInf;
           }
         }
-        // P and dS, bf16, as A operands of the two 16-row steps: step ks takes
-        // accumulator rows 8ks .. 8ks+7 of this lane
-        u32x4_t pa[2], da[2];
+        // per 16-row step ks (accumulator rows 8ks .. 8ks+7 of this lane,
+        // query rows rb + 8(r/4) + 4h + r%4): P (dV) or dS (dK) in bf16 as
+        // the A operand, then dV += P^T dO or dK += dS^T Q
+        const char* bt = DK ? qt : gt;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          uint32_t pw[4], dw[4];
+          uint32_t pw[4];
 #pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const int r = 8 * ks + 2 * e2;
-            const float p0 = fast_exp2(fmaf(s[r], c2, -l2[r]));
-            const float p1 = fast_exp2(fmaf(s[r + 1], c2, -l2[r + 1]));
-            pw[e2] = pack_bf16x2(p0, p1);
-            dw[e2] = pack_bf16x2(p0 * (dp[r] - dl[r]), p1 * (dp[r + 1] - dl[r + 1]));
+          for (int q = 0; q < 2; ++q) {
+            const int q4 = 2 * ks + q;
+            const f32x4_t x4 = *(const f32x4_t*)&LD[P][0][rb + 8 * q4 + 4 * h];
+            f32x4_t y4 = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (DK) y4 = *(const f32x4_t*)&LD[P][1][rb + 8 * q4 + 4 * h];
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+              const int r = 4 * q4 + 2 * e2;
+              const float l0 = x4[2 * e2] == kNegInf ? __builtin_inff() : x4[2 * e2] * kLog2e;
+              const float l1 = x4[2 * e2 + 1] == kNegInf ? __builtin_inff() : x4[2 * e2 + 1] * kLog2e;
+              const float p0 = fast_exp2(fmaf(s[r], c2, -l0));
+              const float p1 = fast_exp2(fmaf(s[r + 1], c2, -l1));
+              if constexpr (DK)
+                pw[2 * q + e2] = pack_bf16x2(p0 * (dp[r] - y4[2 * e2]), p1 * (dp[r + 1] - y4[2 * e2 + 1]));
+              else
+                pw[2 * q + e2] = pack_bf16x2(p0, p1);
+            }
           }
-          pa[ks] = (u32x4_t){pw[0], pw[1], pw[2], pw[3]};
-          da[ks] = (u32x4_t){dw[0], dw[1], dw[2], dw[3]};
-        }
-        // dV += P^T dO and dK += dS^T Q over the block's 32 rows
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
+          const u32x4_t pa = {pw[0], pw[1], pw[2], pw[3]};
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
-            const u32x2_t y0 = ds_read_tr(gt + 4096 * ks + tro[db][0]);
-            const u32x2_t y1 = ds_read_tr(gt + 4096 * ks + tro[db][1]);
-            const u32x2_t z0 = ds_read_tr(qt + 4096 * ks + tro[db][0]);
-            const u32x2_t z1 = ds_read_tr(qt + 4096 * ks + tro[db][1]);
-            dva[db] = mfma32x32x16(as_bf16x8(pa[ks]), as_bf16x8((u32x4_t){y0[0], y0[1], y1[0], y1[1]}),
-                                   dva[db]);
-            dka[db] = mfma32x32x16(as_bf16x8(da[ks]), as_bf16x8((u32x4_t){z0[0], z0[1], z1[0], z1[1]}),
-                                   dka[db]);
+            const u32x2_t y0 = ds_read_tr(bt + 4096 * ks + tro[db][0]);
+            const u32x2_t y1 = ds_read_tr(bt + 4096 * ks + tro[db][1]);
+            acc[db] = mfma32x32x16(as_bf16x8(pa), as_bf16x8((u32x4_t){y0[0], y0[1], y1[0], y1[1]}),
+                                   acc[db]);
           }
         }
       }
     };
     const std::integral_constant<int, 0> even;
     const std::integral_constant<int, 1> odd;
-    for (int idx = 0; idx < n; idx += 2) {
-      step(even, idx);
-      if (idx + 1 < n) step(odd, idx + 1);
+    for (int x = 0; x < nst; x += 2) {
+      step(even, x);
+      if (x + 1 < nst) step(odd, x + 1);
     }
   }
 
-  // sum the two row halves: rh = 1 leaves its partials in LDS, rh = 0 adds
-  // them and stores; partial layout [kh][tensor][db][r][lane]
-  wait_vmem();
-  __syncthreads();
-  float* red = reinterpret_cast<float*>(Qs);  // 2 x 2 x 4 x 16 x 64 floats = 64 KB
-  if (rh == 1) {
+  float* dst = DK ? a.dk + b * a.ks0 + kvh * a.ks1 : a.dv + b * a.vs0 + kvh * a.vs1;
+  const int64_t ds2 = DK ? a.ks2 : a.vs2;
+  const float mul = DK ? a.scale : 1.f;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        red[(((kh * 2 + 0) * 4 + db) * 16 + r) * 64 + lane] = dka[db][r];
-        red[(((kh * 2 + 1) * 4 + db) * 16 + r) * 64 + lane] = dva[db][r];
-      }
-  }
-  __syncthreads();
-  if (rh == 0) {
-    float* dkp = a.dk + b * a.ks0 + kvh * a.ks1;
-    float* dvp = a.dv + b * a.vs0 + kvh * a.vs1;
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kr = c0 + 32 * kh + 8 * (r >> 2) + 4 * h + (r & 3);
-        const float xk = dka[db][r] + red[(((kh * 2 + 0) * 4 + db) * 16 + r) * 64 + lane];
-        const float xv = dva[db][r] + red[(((kh * 2 + 1) * 4 + db) * 16 + r) * 64 + lane];
-        if (kr < a.Nk) {
-          dkp[(int64_t)kr * a.ks2 + 32 * db + l32] = a.scale * xk;
-          dvp[(int64_t)kr * a.vs2 + 32 * db + l32] = xv;
-        }
-      }
-  }
+    for (int r = 0; r < 16; ++r) {
+      const int kr = c0 + 32 * kh + 8 * (r >> 2) + 4 * h + (r & 3);
+      if (kr < a.Nk) dst[(int64_t)kr * ds2 + 32 * db + l32] = mul * acc[db][r];
+    }
 }
 
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
@@ -605,9 +590,13 @@ hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream) {
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  const int64_t nkv = (int64_t)a.B * a.Hkv * a.nkt;
-  if (nkv > 0)
-    hipLaunchKernelGGL(bwd_dkdv_kernel, dim3((unsigned)nkv), dim3(NT), 0, stream, a);
+  const int64_t nkv = (int64_t)a.B * a.Hkv * ((a.nkt + 1) / 2);  // key-tile pairs
+  if (nkv > 0) {
+    bwd_kv_kernel<false><<<dim3((unsigned)nkv), dim3(NT), 0, stream>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    bwd_kv_kernel<true><<<dim3((unsigned)nkv), dim3(NT), 0, stream>>>(a);
+  }
   return hipGetLastError();
 }
 

@@ -337,6 +337,7 @@ __global__ void __launch_bounds__(NT, 2) bwd_kv_kernel(BackwardArgs a) {
   __shared__ __attribute__((aligned(16))) float LD[2][2][SR];  // [buffer][lse, delta][row]
   __shared__ uint16_t ilist[kBackwardMaxTiles];  // (query tile << 2) | keeps of the two key tiles
   __shared__ int wcount[4];
+  static_assert((kBackwardMaxTiles << 2) <= 65536, "a list entry holds the query tile in 14 bits");
 
   const int t = threadIdx.x;
   const int lane = t & 63;

@@ -84,6 +84,8 @@ SHAPES = [
     dict(B=2, Hq=4, Hkv=2, Nq=130, Nk=333, causal=True),
     dict(B=1, Hq=2, Hkv=2, Nq=200, Nk=129, causal=False),
     dict(B=1, Hq=1, Hkv=1, Nq=1, Nk=1, causal=True),
+    # eight query heads per KV head, an odd key-tile count and a ragged last query tile
+    dict(B=1, Hq=8, Hkv=1, Nq=200, Nk=520, causal=True),
 ]
 
 

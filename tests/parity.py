@@ -112,15 +112,16 @@ def masked_reference(q_rows, k, v, keep_el, scale):
 
 
 def prefill_tile_parity(res, inp, w: synth.Workload, lam: float, b: int, h: int, i: int,
-                        tally: Tally, qf=None, kf=None, vf=None):
-    """Compare one (b, h, query tile i) of a GPU prefill result with the oracle."""
+                        tally: Tally, qf=None, kf=None, vf=None, scale=None):
+    """Compare one (b, h, query tile i) of a GPU prefill result with the oracle
+    (softmax scale 1/sqrt(d) unless given)."""
     G = w.Hq // w.Hkv
     kvh = h // G
     r0, r1 = i * w.br, min((i + 1) * w.br, w.Nq)
     q = qf if qf is not None else synth.to_float(inp.q[b, h, r0:r1], w)
     k = kf if kf is not None else synth.to_float(inp.k[b, kvh], w)
     v = vf if vf is not None else synth.to_float(inp.v[b, kvh], w)
-    scale = 1.0 / math.sqrt(w.d)
+    scale = 1.0 / math.sqrt(w.d) if scale is None else scale
     vis = oracle.visible(w.Nq, w.Nk, w.causal, r0, r1 - r0)
     t = oracle.blasst_rows(q, k, v, lam, w.bc, vis, scale)
     gpu_mask = res.mask[b, h, i].cpu().numpy()
@@ -201,10 +202,12 @@ def prefill_twopass_tile_parity(res, inp, w: synth.Workload, lam: float, b: int,
     return pre
 
 
-def decode_row_parity(res, q64, k64, v64, lam: float, bc: int, b: int, hq: int, tally: Tally):
-    """Compare one (b, hq) decode row. q64 [d]; k64 [Nk,d]; v64 [Nk,dv] (float64)."""
+def decode_row_parity(res, q64, k64, v64, lam: float, bc: int, b: int, hq: int, tally: Tally,
+                      scale=None):
+    """Compare one (b, hq) decode row. q64 [d]; k64 [Nk,d]; v64 [Nk,dv] (float64);
+    softmax scale 1/sqrt(d) unless given."""
     nk = k64.shape[0]
-    scale = 1.0 / math.sqrt(q64.shape[0])
+    scale = 1.0 / math.sqrt(q64.shape[0]) if scale is None else scale
     t = oracle.blasst_rows(q64[None], k64, v64, lam, bc, np.ones((1, nk), bool), scale)
     gpu_mask = res.mask[b, hq].cpu().numpy()
     flips = check_mask_row(gpu_mask, t.mask, t.gap, lam, tally, f"b{b} h{hq}")

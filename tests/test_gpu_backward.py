@@ -66,7 +66,7 @@ def _dev(x, dtype=None):
     return t.cuda() if dtype is None else t.to(dtype).cuda()
 
 
-def _backward(w, inp, fwd, g_np, out="fp32", rows=None):
+def _backward(w, inp, fwd, g_np, out="fp32", rows=None, scale=None):
     """GPU backward with the oracle's forward (mask, lse, out) as its inputs.
     rows: optional (mask, lse, out) arrays for the whole call (sampled runs)."""
     q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
@@ -74,7 +74,8 @@ def _backward(w, inp, fwd, g_np, out="fp32", rows=None):
     od = torch.float32 if out == "fp32" else torch.bfloat16
     g = torch.from_numpy(g_np).view(torch.bfloat16).cuda()
     dq, dk, dv = A.prefill_backward(q, k, v, _dev(o, torch.float32).to(od), g,
-                                    _dev(lse, torch.float32), _dev(mask), causal=w.causal)
+                                    _dev(lse, torch.float32), _dev(mask), causal=w.causal,
+                                    scale=scale)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -111,6 +112,25 @@ def test_prefill_backward_small(shape, lam, gain, out):
     _check("dk", dk, rk, mk, label)
     _check("dv", dv, rv, mv, label)
 
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.2])
+def test_prefill_backward_explicit_scale(scale):
+    """A softmax scale other than 1/sqrt(d): the forward (oracle) and the
+    backward both use it; dq and dk carry it as a factor."""
+    w = synth.small_workload("prefill", B=1, Hq=4, Hkv=2, Nq=300, Nk=520, d=128, dtype="bf16",
+                             br=128, bc=64, gain=6.0, seed=58, window=32)
+    inp = synth.make_inputs(w)
+    qf, kf, vf = (synth.to_float(x, w) for x in (inp.q, inp.k, inp.v))
+    fwd = oracle.prefill(qf, kf, vf, 1e-2, True, 128, 64, scale=scale)
+    assert (fwd.mask == 0).any()
+    g_np = _dout(np.random.default_rng(8), (w.B, w.Hq, w.Nq, w.dv))
+    dq, dk, dv = _backward(w, inp, fwd, g_np, scale=scale)
+    rq, rk, rv, mq, mk, mv = oracle.prefill_backward(qf, kf, vf, synth.to_float(g_np, w), fwd.mask,
+                                                     True, 128, 64, scale=scale, magnitudes=True)
+    _check("dq", dq, rq, mq, f"scale={scale}")
+    _check("dk", dk, rk, mk, f"scale={scale}")
+    _check("dv", dv, rv, mv, f"scale={scale}")
 
 def test_prefill_backward_block_sparse():
     """A block-sparse forward (the oracle's) whose set leaves the first query

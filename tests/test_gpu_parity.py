@@ -42,24 +42,25 @@ def _prefill(inp, w, lam, out="native", **kw):
     return r
 
 
-def _decode(inp, w, lam, out="native", workspace=None):
+def _decode(inp, w, lam, out="native", workspace=None, scale=None):
     q, k = to_device(inp.q, w), to_device(inp.k, w)
     v = to_device(inp.v, w) if inp.v is not None else None
-    r = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv, out_dtype=OUT.get(out), workspace=workspace)
+    r = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv, out_dtype=OUT.get(out), workspace=workspace,
+                 scale=scale)
     torch.cuda.synchronize()
     return r
 
 
-def _check_prefill_full(w, lam, label, out="native"):
+def _check_prefill_full(w, lam, label, out="native", scale=None):
     inp = synth.make_inputs(w)
-    res = _prefill(inp, w, lam, out)
+    res = _prefill(inp, w, lam, out, scale=scale)
     tally = Tally()
     nqt = synth.n_tiles(w.Nq, w.br)
     stats_mask = res.mask.cpu().numpy()
     for b in range(w.B):
         for h in range(w.Hq):
             for i in range(nqt):
-                prefill_tile_parity(res, inp, w, lam, b, h, i, tally)
+                prefill_tile_parity(res, inp, w, lam, b, h, i, tally, scale=scale)
     st = res.stats.cpu().numpy()
     assert np.array_equal(st[..., 0], (stats_mask != 2).sum(axis=(2, 3)))
     assert np.array_equal(st[..., 1], (stats_mask == 1).sum(axis=(2, 3)))
@@ -156,9 +157,9 @@ def test_prefill_qwen7b_n131072(lam, gain):
 
 # ----------------------------------------------------------------------------- decode
 
-def _check_decode(w, lam, pairs=None, out="bf16"):
+def _check_decode(w, lam, pairs=None, out="bf16", scale=None):
     inp = synth.make_inputs(w)
-    res = _decode(inp, w, lam, out)
+    res = _decode(inp, w, lam, out, scale=scale)
     tally = Tally()
     if pairs is None:
         pairs = [(b, kvh) for b in range(w.B) for kvh in range(w.Hkv)]
@@ -166,7 +167,8 @@ def _check_decode(w, lam, pairs=None, out="bf16"):
         kf = synth.to_float(inp.k[b, kvh], w)
         vf = kf[:, :w.dv] if inp.v is None else synth.to_float(inp.v[b, kvh], w)
         for hq in range(kvh * w.G, (kvh + 1) * w.G):
-            decode_row_parity(res, synth.to_float(inp.q[b, hq], w), kf, vf, lam, w.bc, b, hq, tally)
+            decode_row_parity(res, synth.to_float(inp.q[b, hq], w), kf, vf, lam, w.bc, b, hq, tally,
+                              scale=scale)
     m = res.mask.cpu().numpy()
     st = res.stats.cpu().numpy()
     nkt = m.shape[2]
@@ -414,3 +416,35 @@ def test_strided_layout_matches_contiguous():
     torch.cuda.synchronize()
     assert torch.equal(ref.out.view(torch.int16), got.out.view(torch.int16))
     assert torch.equal(ref.mask, got.mask)
+
+
+# ----------------------------------------------------------------------------- explicit scale
+
+# Every entry point takes a softmax scale (<= 0 means 1/sqrt(d_qk)); a sharper
+# and a flatter scale than the default, with drops, on each kernel.
+@pytest.mark.parametrize("scale", [0.05, 0.2])
+def test_prefill_bf16_explicit_scale(scale):
+    w = synth.small_workload("prefill", d=128, dtype="bf16", br=128, bc=64, gain=6.0, seed=34,
+                             window=32, B=1, Hq=2, Hkv=1, Nq=300, Nk=700, causal=True)
+    _check_prefill_full(w, 1e-2, f"bf16 scale={scale}", scale=scale)
+
+
+@pytest.mark.parametrize("scale", [0.05, 0.3])
+def test_prefill_fp32_explicit_scale(scale):
+    w = synth.small_workload("prefill", d=64, dtype="fp32", br=64, bc=64, gain=6.0, seed=35,
+                             window=32, B=1, Hq=2, Hkv=1, Nq=200, Nk=333, causal=True)
+    _check_prefill_full(w, 1e-2, f"fp32 scale={scale}", scale=scale)
+
+
+@pytest.mark.parametrize("scale", [0.03, 0.2])
+def test_decode_gqa_explicit_scale(scale):
+    w = synth.small_workload("decode", d=128, dtype="bf16", bc=64, gain=6.0, seed=56,
+                             window=64, B=2, Hq=8, Hkv=2, Nk=1000)
+    _check_decode(w, 1e-2, scale=scale)
+
+
+@pytest.mark.parametrize("scale", [0.02, 0.1])
+def test_decode_mla_explicit_scale(scale):
+    w = synth.small_workload("decode_mla", d=576, dv=512, dtype="bf16", bc=64, gain=6.0, seed=57,
+                             window=64, B=1, Hq=128, Hkv=1, Nk=2000)
+    _check_decode(w, 1e-2, scale=scale)

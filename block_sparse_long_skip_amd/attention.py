@@ -32,7 +32,7 @@ STATUS = {
 EXPORTED = ("blasst_attn_prefill", "blasst_attn_prefill_masked", "blasst_attn_prefill_backward",
             "blasst_prefill_backward_workspace_size", "blasst_quantize_mxfp4",
             "blasst_attn_prefill_twopass", "blasst_prefill_twopass_workspace_size",
-            "blasst_attn_decode",
+            "blasst_attn_decode", "blasst_attn_decode_workspace_size",
             "blasst_decode_workspace_size", "blasst_status_string", "blasst_last_error",
             "blasst_version")
 
@@ -113,6 +113,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.blasst_decode_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int,
                                                  ctypes.c_int, ctypes.c_int,
                                                  ctypes.POINTER(ctypes.c_size_t)]
+    lib.blasst_attn_decode_workspace_size.restype = ctypes.c_size_t
+    lib.blasst_attn_decode_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int,
+                                                      ctypes.c_int]
     lib.blasst_status_string.restype = ctypes.c_char_p
     lib.blasst_status_string.argtypes = [ctypes.c_int]
     lib.blasst_last_error.restype = ctypes.c_char_p

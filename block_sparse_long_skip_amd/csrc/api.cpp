@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -306,6 +307,19 @@ blasst_status_t blasst_decode_workspace_size(const blasst_shape_t* shape, blasst
   if (st != BLASST_OK) return st;
   *bytes = decode_workspace(*shape, kind, bc);
   return ok();
+}
+
+size_t blasst_attn_decode_workspace_size(const blasst_shape_t* shape, blasst_dtype_t dtype,
+                                         int bc) {
+  // The cache kind follows from the sizes: only a latent cache has d_v < d_qk.
+  size_t bytes = 0;
+  if (!shape) {
+    fail(BLASST_E_NULL, "shape is NULL");
+    return SIZE_MAX;
+  }
+  const int has_v = shape->d_v < shape->d_qk ? 0 : 1;
+  if (blasst_decode_workspace_size(shape, dtype, has_v, bc, &bytes) != BLASST_OK) return SIZE_MAX;
+  return bytes;
 }
 
 blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const void* v_cache,

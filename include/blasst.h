@@ -337,6 +337,17 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
 blasst_status_t blasst_decode_workspace_size(const blasst_shape_t* shape, blasst_dtype_t dtype,
                                              int has_v_cache, int bc, size_t* bytes);
 
+/*
+ * The same query in the form the hot-path contract names: the cache kind is
+ * taken from the sizes (d_v < d_qk is a latent cache whose values are the
+ * first d_v features of each key, v_cache NULL; otherwise a separate v_cache).
+ * Returns the workspace bytes blasst_attn_decode needs (0 when none), or
+ * SIZE_MAX when the shape, dtype or tile size has no decode kernel or shape is
+ * NULL; blasst_last_error() then says why. Launches nothing.
+ */
+size_t blasst_attn_decode_workspace_size(const blasst_shape_t* shape, blasst_dtype_t dtype,
+                                         int bc);
+
 /* Static text for a status code. */
 const char* blasst_status_string(blasst_status_t status);
 

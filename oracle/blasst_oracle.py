@@ -403,19 +403,6 @@ def decode(q: np.ndarray, k: np.ndarray, v: Optional[np.ndarray], lam: float, bc
     return OracleResult(out, lse, mask, gap, stats)
 
 
-def naive_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, causal: bool,
-                    scale: Optional[float] = None) -> np.ndarray:
-    """Textbook softmax(scale * q k^T) v for one head: q [Nq,d], k [Nk,d], v [Nk,dv]."""
-    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
-    if scale is None:
-        scale = default_scale(q.shape[1])
-    s = scale * (q @ k.T)
-    s = np.where(visible(q.shape[0], k.shape[0], causal), s, -np.inf)
-    s = s - s.max(axis=1, keepdims=True)
-    p = np.exp(s)
-    return (p @ v) / p.sum(axis=1, keepdims=True)
-
-
 def expand_tile_mask(mask_row: np.ndarray, br: int, bc: int, nq: int, nk: int) -> np.ndarray:
     """[nQt, nKt] tile mask -> [nq, nk] boolean 'kept' per (query, key) pair."""
     kept = (np.asarray(mask_row) == MASK_KEPT)
@@ -566,6 +553,6 @@ __all__ = [
     "block_sparse_rows", "prefill_masked", "prefill_backward",
     "round_to_e2m1", "mx_quantize_fp4", "mx_dequantize_fp4", "twopass_tile", "prefill_twopass",
     "MX_BLOCK", "E2M1_MAGNITUDES",
-    "decode_row", "decode", "naive_attention", "expand_tile_mask", "masked_dense_attention",
+    "decode_row", "decode", "expand_tile_mask", "masked_dense_attention",
     "OracleResult", "TileRowResult", "MASK_SKIPPED", "MASK_KEPT", "MASK_NOT_VISITED",
 ]

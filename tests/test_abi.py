@@ -393,6 +393,28 @@ def test_decode_workspace_size():
     assert lib.blasst_decode_workspace_size(ctypes.byref(sh), BF16, 1, 64, None) == 1
 
 
+def test_attn_decode_workspace_size_contract_form():
+    """blasst_attn_decode_workspace_size(shape, dtype, bc) takes the cache kind
+    from the sizes and returns the same bytes as the status-returning query;
+    SIZE_MAX, with the reason in blasst_last_error, for anything with no kernel."""
+    lib = A.load_library()
+    size_max = ctypes.c_size_t(-1).value
+    for sh, has_v in [(_shape(Hq=8, Hkv=2, Nq=1, Nk=1000), True),
+                      (_shape(B=3, Hq=128, Hkv=1, Nq=1, Nk=9000, d=576, dv=512), False),
+                      (_shape(B=1, Hq=20, Hkv=2, Nq=1, Nk=300, d=576, dv=512), False)]:
+        st, n = _ws_size(sh, has_v)
+        assert st == 0
+        assert lib.blasst_attn_decode_workspace_size(ctypes.byref(sh), BF16, 64) == n
+    bad = [(_shape(Hq=8, Hkv=2, Nq=2, Nk=1000), BF16, 64),            # len_q != 1
+           (_shape(Hq=8, Hkv=2, Nq=1, Nk=1000, d=96, dv=96), BF16, 64),  # no kernel
+           (_shape(Hq=8, Hkv=2, Nq=1, Nk=1000), FP32, 64),            # no fp32 decode
+           (_shape(Hq=8, Hkv=2, Nq=1, Nk=1000), BF16, 32)]            # tile size
+    for sh, dt, bc in bad:
+        assert lib.blasst_attn_decode_workspace_size(ctypes.byref(sh), dt, bc) == size_max
+        assert _err() != ""
+    assert lib.blasst_attn_decode_workspace_size(None, BF16, 64) == size_max
+
+
 def test_binding_has_no_cpu_fallback():
     """The Python binding refuses CPU tensors instead of computing anything."""
     import torch

@@ -64,8 +64,16 @@ def _check_prefill_full(w, lam, label, out="native", scale=None):
     st = res.stats.cpu().numpy()
     assert np.array_equal(st[..., 0], (stats_mask != 2).sum(axis=(2, 3)))
     assert np.array_equal(st[..., 1], (stats_mask == 1).sum(axis=(2, 3)))
-    tally.check(w.dtype, label, out_bf16=res.out.dtype == torch.bfloat16)
+    _check_tally(tally, w, label, res.out.dtype == torch.bfloat16)
     return res
+
+
+def _check_tally(tally, w, label, out_bf16):
+    """The bar of the parity helpers; at gain 1 (the workloads as specified)
+    bf16 outputs must also meet the plain bar against the unrounded oracle."""
+    tally.check(w.dtype, label, out_bf16=out_bf16)
+    if out_bf16 and w.gain == 1.0:
+        tally.check(w.dtype, label + " (unrounded reference)", out_bf16=True, strict=True)
 
 
 # ----------------------------------------------------------------------------- prefill fp32
@@ -134,7 +142,7 @@ def _prefill_sampled(cfg, lam, gain, heads, per_head, seed, out="bf16"):
     assert ((m == 2) == (np.arange(nkt)[None, :] > last_vis[:, None])[None, None]).all()
     st = res.stats.cpu().numpy()
     assert np.array_equal(st[..., 1], (m == 1).sum(axis=(2, 3)))
-    tally.check(w.dtype, f"workload {cfg} lam={lam} g={gain}", out_bf16=out == "bf16")
+    _check_tally(tally, w, f"workload {cfg} lam={lam} g={gain}", out == "bf16")
     return res
 
 
@@ -178,7 +186,7 @@ def _check_decode(w, lam, pairs=None, out="bf16", scale=None):
         for kvh in range(w.Hkv):
             grp = m[b, kvh * w.G:(kvh + 1) * w.G]
             assert (st[b, kvh * w.G:(kvh + 1) * w.G, 2] == (grp == 1).any(axis=0).sum()).all()
-    tally.check(w.dtype, f"decode {w.name} lam={lam} g={w.gain}", out_bf16=out == "bf16")
+    _check_tally(tally, w, f"decode {w.name} lam={lam} g={w.gain}", out == "bf16")
     return res
 
 

@@ -176,6 +176,33 @@ def pin_masked_sdpa(orc):
     assert n_skipped > 0, "fixture must exercise dropped tiles"
 
 
+def pin_masked_dense_attention(orc):
+    """Softmax restricted to a set of (query, key) pairs, the reference the GPU
+    parity checks fall back to on near-threshold flips: the tile-to-pair
+    expansion against a hand-built fixture, then the restricted softmax
+    against torch SDPA (float64) with the same boolean mask, and its lse
+    against torch.logsumexp of the allowed scores."""
+    g = _load("tile_expansion.json")
+    sh = g["shape"]
+    el = orc.expand_tile_mask(np.array(g["tile_mask"], np.uint8), sh["br"], sh["bc"], sh["Nq"],
+                              sh["Nk"])
+    assert el.tolist() == g["expect"], g["derivation"]
+    rng = np.random.default_rng(23)
+    for (Nq, Nk, d, dv, causal) in [(9, 9, 4, 3, True), (6, 17, 8, 8, True), (11, 5, 4, 6, False)]:
+        q, k, v = (rng.standard_normal((n, m)) * 2.0 for n, m in ((Nq, d), (Nk, d), (Nk, dv)))
+        keep = rng.random((Nq, Nk)) < 0.5
+        vis = np.arange(Nk)[None, :] <= np.arange(Nq)[:, None] + (Nk - Nq) if causal \
+            else np.ones((Nq, Nk), bool)
+        keep[np.arange(Nq), np.arange(Nq) + (Nk - Nq) if causal else 0] = True  # a pair per row
+        sc = 0.7
+        out, lse = orc.masked_dense_attention(q, k, v, keep, causal, sc)
+        am = keep & vis
+        ref = _sdpa(q[None], k[None], v[None], False, sc, attn_mask=am[None])[0]
+        assert np.abs(out - ref).max() < 1e-12
+        s = np.where(am, sc * (q @ k.T), -np.inf)
+        assert np.abs(lse - torch.logsumexp(torch.from_numpy(s), dim=-1).numpy()).max() < 1e-12
+
+
 def _prefix_max_closed_form(q, k, lam, causal, br, bc, scale):
     """mask[i,j] = j==0 or max_r (tilemax[r,j] - max_{t<j} tilemax[r,t]) >= thr, from dense S."""
     B, Hq, Nq, d = q.shape
@@ -663,7 +690,8 @@ def pin_twopass_map_and_output(orc):
 
 
 PINS = [pin_hand_example, pin_row_aggregation, pin_tie, pin_causal_visibility,
-        pin_lambda0_sdpa, pin_bottom_right_causal, pin_masked_sdpa, pin_closed_form_mask,
+        pin_lambda0_sdpa, pin_bottom_right_causal, pin_masked_sdpa, pin_masked_dense_attention,
+        pin_closed_form_mask,
         pin_brute_force, pin_decode_sdpa, pin_block_sparse_sdpa, pin_block_sparse_kept,
         pin_block_sparse_full_set, pin_block_sparse_brute, pin_backward_autograd,
         pin_backward_finite_difference, pin_mxfp4_golden, pin_mxfp4_brute_force,
@@ -791,6 +819,11 @@ MUTATIONS = {
     "mx_no_clamp": ("np.minimum(np.rint(a / ulp) * ulp, E2M1_MAX)", "np.rint(a / ulp) * ulp"),
     "mx_sign_dropped": ("code |= (np.signbit(blk).astype(np.uint8) << 3)", "code |= 0"),
     "twopass_decides_on_exact_scores": ("pre = prefill_tile(qd, kd, v,", "pre = prefill_tile(q, k, v,"),
+    "tile_expansion_transposed": ("el = np.repeat(np.repeat(kept, br, axis=0), bc, axis=1)",
+                                  "el = np.repeat(np.repeat(kept, bc, axis=0), br, axis=1)"),
+    "restricted_softmax_keep_ignored": ("allowed = keep & visible(q.shape[0], k.shape[0], causal)",
+                                        "allowed = visible(q.shape[0], k.shape[0], causal)"),
+    "restricted_softmax_lse_without_max": ("(mx + np.log(den))[:, 0]", "(np.log(den))[:, 0]"),
     "twopass_pass2_over_visible": ("pre.mask == MASK_KEPT, 0.0,", "pre.mask != MASK_NOT_VISITED, 0.0,"),
 }
 

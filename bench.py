@@ -5,9 +5,10 @@
 
 A step is one skip-softmax prefill call (the whole hot path: QK^T on MFMA, the
 per-tile drop vote, V loads and P.V for kept tiles, the output, lse, the tile
-mask and the statistics) over the Llama-3.1-8B-shaped layer: causal, B=1,
-32 query / 8 KV heads, N=32768, d=128, bf16, 128x64 tiles, seeded synthetic
-inputs already resident in HBM. The line printed on stdout carries:
+mask and the statistics) over the Qwen2.5-7B-shaped long prefill layer, the
+largest workload that runs on one GPU: causal, B=1, 28 query / 4 KV heads,
+N=131072, d=128, bf16, 128x64 tiles, lambda=1e-3, seeded synthetic inputs
+already resident in HBM. The line printed on stdout carries:
 
   value        dense-equivalent TFLOP/s = 2 (d + dv) B Hq P / t, where P is the
                number of visible (query, key) pairs (causal: N(N+1)/2); the
@@ -18,28 +19,34 @@ inputs already resident in HBM. The line printed on stdout carries:
                from HIP events on the launch stream; HBM traffic per launch
                from rocprofv3 counters when the committed counter summary
                matches the current kernel source
-  lambda_sweep every lambda of the workload, at gain 1 (the workload as
-               specified, nothing is dropped) and at the supplementary gain 6
-               (planted boosts scaled so tiles are dropped): TFLOP/s, skip
-               fraction and speed-up over lambda = 0
+  lambda_sweep the headline layer at every lambda at gain 1 (the workload as
+               specified, nothing is dropped) and at the supplementary gain 8:
+               TFLOP/s, skip fraction (overall and per KV head with its needle
+               rate) and speed-up over lambda = 0
+  skip_regime  the same shape with every KV head at 0.1% needles, gain 8
+               (supplementary): one-pass and two-pass against lambda = 0
+  prefill_llama8b_n32768
+               the Llama-3.1-8B-shaped layer (N=32768, 32/8 heads) the same way,
+               at gains 1 and 6
   block_sparse_prefill
-               the same layer restricted to seeded block sets shaped like those of
-               block-sparse prefill methods (sink tile, local window, vertical
-               columns, scattered blocks) at densities 0.1 and 0.25: algorithmic
-               TFLOP/s of the selected work and speed-up over dense lambda = 0
+               the Llama-shaped layer restricted to seeded block sets shaped like
+               those of block-sparse prefill methods (sink tile, local window,
+               vertical columns, scattered blocks) at densities 0.1 and 0.25:
+               algorithmic TFLOP/s of the selected work and speed-up over dense
+               lambda = 0
   prefill_backward
-               dq, dk, dv of the same layer with the forward's mask held fixed:
-               algorithmic TFLOP/s (5 products per kept tile) against the peak
+               dq, dk, dv of the Llama-shaped layer with the forward's mask held
+               fixed: algorithmic TFLOP/s (5 products per kept tile)
   prefill_twopass
-               the two-pass variant on the same layer (MXFP4 max pre-pass, then
-               exact attention over the kept tiles): time against the one-pass
-               call, the pre-pass share, agreement of its map with the exact
-               rule's mask, and FP4 TFLOP/s of the pre-pass
+               the two-pass variant on the Llama-shaped layer (MXFP4 max
+               pre-pass, then exact attention over the kept tiles): time against
+               the one-pass call, the pre-pass share, agreement of its map with
+               the exact rule's mask, and FP4 TFLOP/s of the pre-pass
   decode       the batch-32 GQA decode over 65536 keys and the batch-16 MLA
                decode over 32768 latent keys: GB/s of the bytes actually read
                (K always, V only for tiles some head keeps) against 8 TB/s
   cpu_baseline the CPU oracle timed on a bounded sample of query tiles of the
-               same workload (a reported baseline, not a target)
+               headline layer (a reported baseline, not a target)
 """
 from __future__ import annotations
 
@@ -91,6 +98,9 @@ def parse():
     ap.add_argument("--only", choices=["prefill", "prefill_masked", "backward", "twopass", "decode_gqa",
                                        "decode_mla", "copy"],
                     help="launch only this kernel --steps times (for rocprofv3 counter passes)")
+    ap.add_argument("--workload", choices=["qwen7b", "llama8b"], default="qwen7b",
+                    help="prefill layer of --only prefill: the 131072-long Qwen2.5-7B shape or "
+                         "the 32768-long Llama-3.1-8B shape")
     return ap.parse_args()
 
 
@@ -107,7 +117,8 @@ def to_device(x, w):
 
 def time_calls(fn, steps, warmup):
     """Run fn() warmup times, then time `steps` calls with HIP events on the current
-    stream. Returns (mean ms per call from events, wall ms per step, last result)."""
+    stream. Returns (mean ms per call from events, wall ms per step, last result,
+    median ms per call)."""
     import torch
     res = None
     for _ in range(warmup):
@@ -122,8 +133,10 @@ def time_calls(fn, steps, warmup):
         ends[s].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    ev = sum(a.elapsed_time(b) for a, b in zip(starts, ends)) / steps
-    return ev, wall, res
+    per = sorted(a.elapsed_time(b) for a, b in zip(starts, ends))
+    ev = sum(per) / steps
+    med = per[steps // 2] if steps % 2 else 0.5 * (per[steps // 2 - 1] + per[steps // 2])
+    return ev, wall, res, med
 
 
 def prefill_algorithmic_flops(w, stats):
@@ -148,55 +161,146 @@ def read_traffic(kind: str, sha: str):
 
 # --------------------------------------------------------------------------- legs
 
-def bench_prefill(args):
+HEADLINE_CFG = 4  # the largest single-GPU workload: the Qwen2.5-7B-shaped 131072-long prefill
+SKIP_NEEDLE_RATE = 0.001  # low end of that workload's per-head needle-rate range
+
+
+def skip_regime_workload(w):
+    """The headline shape with every KV head at the low end of its needle-rate
+    range (0.1%): a supplementary input, not one of the listed workloads, where
+    most tiles hold no planted key and the pages' 50-60% skip regime is reached."""
+    from dataclasses import replace
+    return replace(w, name=w.name + "_needles0.1pct", needle_rate=SKIP_NEEDLE_RATE,
+                   needle_rate_range=None)
+
+
+def per_group_skip(w, stats):
+    """Skip fraction per KV head (its query heads pooled), with its needle rate."""
+    from block_sparse_long_skip_amd import synth
+    st = stats.double().cpu()
+    rates = synth.needle_rates(w)
+    out = []
+    for g in range(w.Hkv):
+        vis = st[:, g * w.G:(g + 1) * w.G, 0].sum().item()
+        kept = st[:, g * w.G:(g + 1) * w.G, 1].sum().item()
+        out.append(dict(kv_head=g, needle_rate=round(float(rates[g]), 5),
+                        skip_fraction=round(1.0 - kept / max(vis, 1.0), 4)))
+    return out
+
+
+def prefill_row(w, lam, gain, ms, res, dense, base_ms):
+    alg, visited, kept = prefill_algorithmic_flops(w, res.stats)
+    atf = alg / (ms * 1e-3) / 1e12
+    return dict(gain=gain, lam=lam, ms=round(ms, 4), tflops=round(dense / (ms * 1e-3) / 1e12, 2),
+                algorithmic_tflops=round(atf, 2), frac_mfma=round(atf / PEAK_BF16_TFLOPS, 4),
+                skip_fraction=round(res.skip_fraction, 4),
+                speedup_vs_lam0=round(base_ms / ms, 3) if base_ms else None)
+
+
+def bench_prefill(args, cid, kind, gains, skip_regime=False):
+    """One causal prefill workload: the headline lambda at gain 1 timed over
+    --steps calls (value, roofline), then a lambda sweep at each listed gain
+    (and, with skip_regime, on the low-needle variant, one-pass and two-pass)."""
     import torch
     from block_sparse_long_skip_amd import attention as A
     from block_sparse_long_skip_amd import synth
 
-    w = synth.WORKLOADS[2]
+    w = synth.WORKLOADS[cid]
     log(f"[bench] generating {w.name} (gain 1)")
     inp = synth.make_inputs(w)
     q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
+    del inp
     dense = synth.dense_equivalent_flops(w)
 
-    def call(lam):
-        return A.prefill(q, k, v, lam, causal=True, br=w.br, bc=w.bc)
+    def call(lam, q_=q, k_=k, v_=v):
+        return A.prefill(q_, k_, v_, lam, causal=True, br=w.br, bc=w.bc)
 
-    log(f"[bench] timing prefill lambda={args.lam} steps={args.steps} warmup={args.warmup}")
-    ev_ms, wall_ms, res = time_calls(lambda: call(args.lam), args.steps, args.warmup)
+    log(f"[bench] timing {w.name} lambda={args.lam} steps={args.steps} warmup={args.warmup}")
+    ev_ms, wall_ms, res, med_ms = time_calls(lambda: call(args.lam), args.steps, args.warmup)
     alg, visited, kept = prefill_algorithmic_flops(w, res.stats)
     value = dense / (ev_ms * 1e-3) / 1e12
     achieved = alg / (ev_ms * 1e-3) / 1e12
     sha = source_sha(PREFILL_SOURCES)
-    traffic, tnote = read_traffic("prefill_bf16_llama8b_n32768", sha)
-    out = dict(value=value, ms_per_step=ev_ms, wall_ms_per_step=wall_ms,
-               skip_fraction=1.0 - kept / visited, visited_tiles=int(visited), kept_tiles=int(kept),
+    traffic, tnote = read_traffic(f"prefill_bf16_{kind}", sha)
+    out = dict(workload=w.name, value=value, ms_per_step=ev_ms, median_ms=med_ms,
+               wall_ms_per_step=wall_ms, skip_fraction=1.0 - kept / visited,
+               visited_tiles=int(visited), kept_tiles=int(kept),
                roofline=dict(bound="mfma", achieved=round(achieved, 2), peak=PEAK_BF16_TFLOPS,
                              unit="TFLOP/s", frac=round(achieved / PEAK_BF16_TFLOPS, 4),
                              traffic=traffic, traffic_note=tnote,
                              algorithmic_flops_per_launch=alg,
                              kernel="prefill_bf16_kernel<false>", kernel_source_sha=sha))
+    log(f"[bench]   {w.name}: {ev_ms:.3f} ms (median {med_ms:.3f}), {value:.1f} dense-equivalent "
+        f"TFLOP/s, {achieved / PEAK_BF16_TFLOPS:.3f} of the bf16 peak")
     sweep = []
+    reps = max(3, args.steps // 2)
     if not args.no_sweep:
-        for gain in (1.0, 6.0):
+        for gain in gains:
             if gain != 1.0:
-                log(f"[bench] generating gain {gain}")
+                log(f"[bench] generating {w.name} gain {gain}")
                 gi = synth.make_inputs(w.with_gain(gain))
                 q2, k2, v2 = (to_device(x, w) for x in (gi.q, gi.k, gi.v))
+                del gi
             else:
                 q2, k2, v2 = q, k, v
             base = None
-            for lam in w.lambdas:
-                ms, _, r = time_calls(lambda: A.prefill(q2, k2, v2, lam, causal=True, br=w.br, bc=w.bc),
-                                      max(3, args.steps // 2), args.warmup)
+            for lam in w.lambdas + ((1e-2,) if gain != 1.0 and 1e-2 not in w.lambdas else ()):
+                ms, _, r, _ = time_calls(lambda: call(lam, q2, k2, v2), reps, args.warmup)
                 base = ms if lam == 0.0 else base
-                sweep.append(dict(gain=gain, lam=lam, tflops=round(dense / (ms * 1e-3) / 1e12, 2),
-                                  ms=round(ms, 4), skip_fraction=round(r.skip_fraction, 4),
-                                  speedup_vs_lam0=round(base / ms, 3) if base else None))
+                row = prefill_row(w, lam, gain, ms, r, dense, base)
+                if w.Hkv > 1 and lam > 0:
+                    row["per_kv_head"] = per_group_skip(w.with_gain(gain), r.stats)
+                sweep.append(row)
                 log(f"[bench]   gain {gain} lam {lam}: {ms:.3f} ms, skip {r.skip_fraction:.3f}")
             del q2, k2, v2
+            torch.cuda.empty_cache()
     out["sweep"] = sweep
+    if skip_regime and not args.no_sweep:
+        out["skip_regime"] = bench_skip_regime(args, w, dense, reps)
+    del q, k, v, res
+    torch.cuda.empty_cache()
     return out, w
+
+
+def bench_skip_regime(args, w, dense, reps):
+    """The low-needle variant of the workload at gain 8: one-pass at every
+    lambda, and the two-pass variant (MXFP4 max pre-pass, then exact attention
+    over the kept tiles) beside it."""
+    import torch
+    from block_sparse_long_skip_amd import attention as A
+    from block_sparse_long_skip_amd import synth
+
+    ws_ = skip_regime_workload(w).with_gain(8.0)
+    log(f"[bench] generating {ws_.name} gain 8 (skip regime)")
+    gi = synth.make_inputs(ws_)
+    q, k, v = (to_device(x, ws_) for x in (gi.q, gi.k, gi.v))
+    del gi
+    wsp = torch.empty(A.prefill_twopass_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk),
+                      dtype=torch.uint8, device="cuda")
+    rows, base = [], None
+    for lam in (0.0, 1e-3, 1e-2):
+        ms, _, r, _ = time_calls(lambda: A.prefill(q, k, v, lam, causal=True), reps, args.warmup)
+        base = ms if lam == 0.0 else base
+        row = prefill_row(ws_, lam, 8.0, ms, r, dense, base)
+        if lam > 0:
+            tms, _, tr, _ = time_calls(lambda: A.prefill_twopass(q, k, v, lam, causal=True,
+                                                                 workspace=wsp), reps, args.warmup)
+            vis = r.mask != 2
+            row["twopass"] = dict(ms=round(tms, 4), speedup_vs_lam0=round(base / tms, 3),
+                                  speedup_vs_one_pass=round(ms / tms, 3),
+                                  skip_fraction=round(tr.skip_fraction, 4),
+                                  map_agreement=round(((tr.mask == r.mask) & vis).sum().item()
+                                                      / max(vis.sum().item(), 1), 5))
+            del tr, vis
+        rows.append(row)
+        log(f"[bench]   skip regime lam {lam}: {ms:.3f} ms, skip {r.skip_fraction:.3f}"
+            + (f", two-pass {row['twopass']['ms']:.3f} ms" if "twopass" in row else ""))
+        del r
+    del q, k, v, wsp
+    torch.cuda.empty_cache()
+    return dict(workload=ws_.name, needle_rate=SKIP_NEEDLE_RATE, gain=8.0,
+                note="supplementary input (not a listed workload): every KV head at the low end "
+                     "of the needle-rate range", rows=rows)
 
 
 def bench_prefill_masked(args, dense_ms):
@@ -220,7 +324,7 @@ def bench_prefill_masked(args, dense_ms):
             bm = torch.from_numpy(synth.block_set(w, density, seed=3)).cuda()
             for lam in (0.0, args.lam):
                 # ~1 ms calls: warm up for tens of milliseconds so the clocks settle
-                ms, _, r = time_calls(lambda: A.prefill_masked(q, k, v, bm, lam, causal=True,
+                ms, _, r, _ = time_calls(lambda: A.prefill_masked(q, k, v, bm, lam, causal=True,
                                                                br=w.br, bc=w.bc),
                                       max(3, args.steps // 2), max(args.warmup, 30))
                 alg, visited, kept = prefill_algorithmic_flops(w, r.stats)
@@ -260,11 +364,11 @@ def bench_twopass(args):
         del inp
         for lam in lams:
             steps, warm = max(3, args.steps // 2), max(args.warmup, 5)
-            one_ms, _, one = time_calls(lambda: A.prefill(q, k, v, lam, causal=True), steps, warm)
-            two_ms, _, two = time_calls(lambda: A.prefill_twopass(q, k, v, lam, causal=True,
+            one_ms, _, one, _ = time_calls(lambda: A.prefill(q, k, v, lam, causal=True), steps, warm)
+            two_ms, _, two, _ = time_calls(lambda: A.prefill_twopass(q, k, v, lam, causal=True,
                                                                   workspace=ws), steps, warm)
             kept = two.mask == 1
-            p2_ms, _, _ = time_calls(lambda: A.prefill_masked(q, k, v, kept, 0.0, causal=True,
+            p2_ms, _, _, _ = time_calls(lambda: A.prefill_masked(q, k, v, kept, 0.0, causal=True,
                                                               want_mask=False, want_stats=False),
                                      steps, warm)
             pre_ms = max(two_ms - p2_ms, 1e-6)
@@ -324,7 +428,7 @@ def bench_backward(args):
         ws = torch.empty(max(1, w.B * w.Hq * w.Nq * 4), dtype=torch.uint8, device="cuda")
         call = lambda: A.prefill_backward(q, k, v, fwd.out, dout, fwd.lse, fwd.mask, causal=True,
                                           workspace=ws)
-        ms, _, _ = time_calls(call, max(3, args.steps // 4), max(args.warmup, 2))
+        ms, _, _, _ = time_calls(call, max(3, args.steps // 4), max(args.warmup, 2))
         kept = fwd.stats[..., 1].double().sum().item()
         flops = 5 * 2.0 * w.br * w.bc * w.d * kept
         dense = 2.5 * synth.dense_equivalent_flops(w)  # 5 products of 2 d FLOPs per visible pair
@@ -408,6 +512,13 @@ def cpu_baseline(args, w):
     except Exception:  # noqa: BLE001
         pass
     cores = threads or len(os.sched_getaffinity(0))
+    cpu_model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                             cpu_model)
+    except OSError:
+        pass
     u = synth.unit_direction(w)
     kf = synth.to_float(synth.k_slice(w, 0, 0, u), w)
     vf = synth.to_float(synth.v_slice(w, 0, 0), w)
@@ -426,9 +537,9 @@ def cpu_baseline(args, w):
             break
     dt = time.perf_counter() - t0
     return dict(value=round(flops / dt / 1e12, 6), unit="TFLOP/s", cores=cores, kind="oracle",
-                sample=f"{len(done)} of {nqt} query tiles of head 0 (random order, seed 12345), "
-                       f"lambda={args.lam}, float64 NumPy, {dt:.1f} s",
-                seconds=round(dt, 2))
+                sample=f"{len(done)} of {nqt} query tiles of head 0 of {w.name} (random order, "
+                       f"seed 12345), lambda={args.lam}, float64 NumPy, {dt:.1f} s",
+                seconds=round(dt, 2), cpu_model=cpu_model)
 
 
 def only(args):
@@ -463,7 +574,8 @@ def only(args):
         torch.cuda.synchronize()
         log(f"[bench] launched backward x {args.steps}")
         return
-    cid = {"prefill": 2, "prefill_masked": 2, "decode_gqa": 3, "decode_mla": 5}[args.only]
+    cid = {"prefill": {"qwen7b": 4, "llama8b": 2}[args.workload], "prefill_masked": 2,
+           "decode_gqa": 3, "decode_mla": 5}[args.only]
     w = synth.WORKLOADS[cid]
     inp = synth.make_inputs(w)
     q, k = to_device(inp.q, w), to_device(inp.k, w)
@@ -500,8 +612,9 @@ def main():
         only(args)
         return
     t_start = time.perf_counter()
-    pre, w = bench_prefill(args)
-    dense_ms = next((x["ms"] for x in pre["sweep"] if x["gain"] == 1.0 and x["lam"] == 0.0), None)
+    pre, w = bench_prefill(args, HEADLINE_CFG, "qwen7b_n131072", gains=(1.0, 8.0), skip_regime=True)
+    llama, _ = bench_prefill(args, 2, "llama8b_n32768", gains=(1.0, 6.0))
+    dense_ms = next((x["ms"] for x in llama["sweep"] if x["gain"] == 1.0 and x["lam"] == 0.0), None)
     masked = None if args.no_masked or dense_ms is None else bench_prefill_masked(args, dense_ms)
     backward = None if args.no_backward else bench_backward(args)
     twopass = None if args.no_twopass else bench_twopass(args)
@@ -520,12 +633,16 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded planted sinks/needles/recent window, gain 1)",
-        "config": {"workload": "prefill_llama8b_n32768: causal B=1 Hq=32 Hkv=8 N=32768 d=128 "
+        "config": {"workload": "prefill_qwen7b_n131072: causal B=1 Hq=28 Hkv=4 N=131072 d=128 "
                                "bf16 128x64 tiles", "lambda": args.lam, "gain": 1.0,
-                   "out_dtype": "bf16", "skip_fraction": round(pre["skip_fraction"], 4)},
+                   "out_dtype": "bf16", "skip_fraction": round(pre["skip_fraction"], 4),
+                   "median_ms": round(pre["median_ms"], 4)},
         "roofline": pre["roofline"],
         "cpu_baseline": cpu,
         "lambda_sweep": pre["sweep"],
+        "skip_regime": pre.get("skip_regime"),
+        "prefill_llama8b_n32768": {k_: llama[k_] for k_ in ("value", "ms_per_step", "median_ms",
+                                                           "roofline", "sweep")},
         "block_sparse_prefill": masked,
         "prefill_backward": backward,
         "prefill_twopass": twopass,

@@ -58,3 +58,16 @@ def test_source_hash_follows_the_text():
     a = bench.source_sha(bench.PREFILL_SOURCES)
     assert a == bench.source_sha(bench.PREFILL_SOURCES)
     assert a != bench.source_sha(bench.PREFILL_SOURCES[:1])
+
+
+def test_headline_is_the_largest_prefill_layer():
+    """The bench line's workload is the 131072-long Qwen2.5-7B-shaped prefill
+    (28/4 heads): 1024 query tiles per head, tile i sees 2(i + 1) key tiles,
+    so 28 * 1024 * 1025 = 29,388,800 visited tiles at lambda = 0."""
+    w = synth.WORKLOADS[bench.HEADLINE_CFG]
+    assert (w.Nq, w.Nk, w.Hq, w.Hkv, w.d, w.causal) == (131072, 131072, 28, 4, 128, True)
+    assert w.Hq * sum(2 * (i + 1) for i in range(w.Nq // w.br)) == 29_388_800
+    assert w.Nq * w.Nk >= max(x.Nq * x.Nk for x in synth.WORKLOADS.values() if x.kind == "prefill")
+    low = bench.skip_regime_workload(w)
+    assert (synth.needle_rates(low) == bench.SKIP_NEEDLE_RATE).all()
+    assert (low.Nq, low.Hq, low.seed) == (w.Nq, w.Hq, w.seed)

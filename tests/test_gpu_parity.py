@@ -123,7 +123,7 @@ def test_prefill_bf16_small(shape, lam, gain, out):
 
 
 def _prefill_sampled(cfg, lam, gain, heads, per_head, seed, out="bf16"):
-    w = synth.WORKLOADS[cfg].with_gain(gain)
+    w = (synth.WORKLOADS[cfg] if isinstance(cfg, int) else cfg).with_gain(gain)
     inp = synth.make_inputs(w)
     res = _prefill(inp, w, lam, out)
     tally = Tally()
@@ -161,6 +161,15 @@ def test_prefill_llama8b_n32768(lam, gain, out):
 @pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 1.0), (1e-3, 8.0)])
 def test_prefill_qwen7b_n131072(lam, gain):
     _prefill_sampled(4, lam, gain, heads=[0, 27], per_head=1, seed=4)
+
+
+@pytest.mark.parametrize("lam", [1e-3, 1e-2])
+def test_prefill_qwen7b_n131072_low_needles(lam):
+    """The benchmark's skip-regime input: the 131072-long layer with every KV
+    head at 0.1% needles and gain 8, where most tiles hold no planted key."""
+    w = synth.WORKLOADS[4].scaled(needle_rate=0.001, needle_rate_range=None)
+    res = _prefill_sampled(w, lam, 8.0, heads=[0, 13, 27], per_head=1, seed=5)
+    assert res.skip_fraction > 0.5
 
 
 # ----------------------------------------------------------------------------- decode

@@ -261,3 +261,38 @@ def sample_qtiles(w: synth.Workload, heads, per_head: int, seed: int):
         extra = rng.choice(nqt, size=min(per_head, nqt), replace=False).tolist()
         out += [(h, i) for i in sorted(set(base + extra))]
     return out
+
+
+def _decode_group_rows(job):
+    """Oracle decode rows of one (batch, KV head) of a generated workload (run in
+    a worker process: the slices are regenerated there from the seed)."""
+    w, b, kvh, lam, scale = job
+    u = synth.unit_direction(w)
+    kf = synth.to_float(synth.k_slice(w, b, kvh, u), w)
+    vf = kf[:, :w.dv] if w.v_is_k_slice else synth.to_float(synth.v_slice(w, b, kvh), w)
+    rows = []
+    for hq in range(kvh * w.G, (kvh + 1) * w.G):
+        q = synth.to_float(synth.q_slice(w, b, hq, u), w).reshape(-1)
+        t = oracle.blasst_rows(q[None], kf, vf, lam, w.bc, np.ones((1, w.Nk), bool), scale)
+        rows.append((hq, t.out[0], t.lse[0], t.mask, t.gap))
+    return b, kvh, rows
+
+
+def oracle_decode_all(w: synth.Workload, lam: float, workers: int = 8, scale=None):
+    """The oracle over every (batch, head) row of a decode workload, in worker
+    processes (spawned: the GPU process is never forked). Returns out, lse,
+    mask, gap arrays shaped like the GPU call's."""
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    scale = 1.0 / math.sqrt(w.d) if scale is None else scale
+    nkt = synth.n_tiles(w.Nk, w.bc)
+    out = np.zeros((w.B, w.Hq, w.dv))
+    lse = np.zeros((w.B, w.Hq))
+    mask = np.zeros((w.B, w.Hq, nkt), np.uint8)
+    gap = np.zeros((w.B, w.Hq, nkt))
+    jobs = [(w, b, kvh, lam, scale) for b in range(w.B) for kvh in range(w.Hkv)]
+    with ProcessPoolExecutor(max_workers=workers, mp_context=mp.get_context("spawn")) as ex:
+        for b, kvh, rows in ex.map(_decode_group_rows, jobs):
+            for hq, o, l_, m, g in rows:
+                out[b, hq], lse[b, hq], mask[b, hq], gap[b, hq] = o, l_, m, g
+    return out, lse, mask, gap

@@ -17,8 +17,8 @@ import torch
 import oracle
 from block_sparse_long_skip_amd import attention as A
 from block_sparse_long_skip_amd import synth
-from parity import (Tally, decode_row_parity, from_device, prefill_masked_tile_parity,
-                    prefill_tile_parity, sample_qtiles, to_device)
+from parity import (Tally, check_mask_row, decode_row_parity, from_device,
+                    prefill_masked_tile_parity, prefill_tile_parity, sample_qtiles, to_device)
 
 pytestmark = pytest.mark.gpu
 
@@ -248,6 +248,84 @@ def test_decode_mla_small(shape, lam, gain, out):
 def test_decode_mla_b16_n32768(lam, gain, out):
     w = synth.WORKLOADS[5].with_gain(gain)
     _check_decode(w, lam, pairs=[(0, 0), (15, 0)], out=out)
+
+
+@pytest.mark.parametrize("cfg,lam", [(3, 1e-2), (5, 1e-2)])
+def test_decode_whole_call_gain6(cfg, lam):
+    """Every (batch, head) row of the batch-32 GQA decode and of the batch-16
+    latent decode at gain 6 against the oracle: the whole mask (exact outside
+    the near-threshold band), every output row and lse, and the statistics."""
+    from parity import check_mask_row, oracle_decode_all
+    w = synth.WORKLOADS[cfg].with_gain(6.0)
+    inp = synth.make_inputs(w)
+    res = _decode(inp, w, lam, "fp32")
+    del inp
+    ref_out, ref_lse, ref_mask, ref_gap = oracle_decode_all(w, lam)
+    gm = res.mask.cpu().numpy()
+    tally = Tally()
+    flipped_rows = []
+    for b in range(w.B):
+        for hq in range(w.Hq):
+            if check_mask_row(gm[b, hq], ref_mask[b, hq], ref_gap[b, hq], lam, tally,
+                              f"b{b} h{hq}").any():
+                flipped_rows.append((b, hq))
+    keep = np.ones((w.B, w.Hq), bool)
+    for (b, hq) in flipped_rows:  # compared in the sampled tests against the GPU's own mask
+        keep[b, hq] = False
+    got = res.out.double().cpu().numpy()
+    got_lse = res.lse.double().cpu().numpy()
+    tally.add(got[keep], ref_out[keep], got_lse[keep] - ref_lse[keep])
+    st = res.stats.cpu().numpy()
+    assert np.array_equal(st[..., 1], (gm == 1).sum(axis=2))
+    groups = gm.reshape(w.B, w.Hkv, w.G, -1)
+    assert np.array_equal(st[..., 2].reshape(w.B, w.Hkv, w.G),
+                          np.repeat((groups == 1).any(axis=2).sum(axis=2)[..., None], w.G, 2))
+    assert res.skip_fraction > 0.25
+    tally.check(w.dtype, f"decode {w.name} whole call lam={lam} g=6 "
+                f"({len(flipped_rows)} rows with band flips)")
+
+
+def test_decode_mla_split_count_invariance():
+    """The latent decode splits the cache over workgroups with a split length T
+    chosen from the batch: a 32768-key sequence runs with T = 4 at batch 1,
+    64 at batch 16, 128 at batch 32 and 256 at batch 64. The same sequence
+    (the cache shared by the whole batch through a zero batch stride, its query
+    at batch index 0) must give the same mask and statistics bit for bit at
+    every T. Outputs differ in rounding only (each split rounds its
+    probabilities to bf16 against its own reference max), so each T's output
+    and lse are held to the bar against the oracle."""
+    w = synth.WORKLOADS[5].with_gain(6.0)
+    u = synth.unit_direction(w)
+    k1 = to_device(synth.k_slice(w, 0, 0, u), w).view(1, 1, w.Nk, w.d)
+    q1 = to_device(np.stack([synth.q_slice(w, 0, h, u) for h in range(w.Hq)]).reshape(w.Hq, w.d), w)
+    lam = 1e-2
+    results = {}
+    for B in (1, 16, 32, 64):
+        q = torch.randn((B, w.Hq, w.d), dtype=torch.float32, device="cuda").to(torch.bfloat16)
+        q[0] = q1
+        k = k1.expand(B, 1, w.Nk, w.d)  # batch stride 0 (batch 1 keeps its own)
+        assert B == 1 or k.stride(0) == 0
+        r = A.decode(q, k, None, lam, dv=w.dv, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        results[B] = (r.out[0].double().cpu().numpy(), r.mask[0].cpu().numpy(),
+                      r.stats[0].cpu().numpy(), r.lse[0].double().cpu().numpy())
+        del q, k, r
+    ref_mask, ref_stats = results[1][1], results[1][2]
+    for B, (_, m, st_, _) in results.items():
+        assert np.array_equal(m, ref_mask), f"mask differs at batch {B}"
+        assert np.array_equal(st_, ref_stats), f"statistics differ at batch {B}"
+    assert (ref_mask == 0).any()
+    kf = synth.to_float(synth.k_slice(w, 0, 0, u), w)
+    rows = [oracle.blasst_rows(synth.to_float(synth.q_slice(w, 0, hq, u), w), kf, kf[:, :w.dv],
+                               lam, w.bc, np.ones((1, w.Nk), bool), 1.0 / math.sqrt(w.d))
+            for hq in range(w.Hq)]
+    for B, (o, m, _, l_) in results.items():
+        tally = Tally()
+        for hq, t in enumerate(rows):
+            flips = check_mask_row(m[hq], t.mask, t.gap, lam, tally, f"B{B} h{hq}")
+            if not flips.any():
+                tally.add(o[hq], t.out[0], np.array([l_[hq] - t.lse[0]]))
+        tally.check(w.dtype, f"latent decode, sequence inside batch {B}")
 
 
 def test_decode_mla_workspace_reuse():

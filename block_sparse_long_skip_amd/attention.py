@@ -32,7 +32,7 @@ STATUS = {
 EXPORTED = ("blasst_attn_prefill", "blasst_attn_prefill_masked", "blasst_attn_prefill_backward",
             "blasst_prefill_backward_workspace_size", "blasst_quantize_mxfp4",
             "blasst_attn_prefill_twopass", "blasst_prefill_twopass_workspace_size",
-            "blasst_attn_decode", "blasst_attn_decode_workspace_size",
+            "blasst_attn_decode", "blasst_attn_decode_noalloc", "blasst_attn_decode_workspace_size",
             "blasst_decode_workspace_size", "blasst_status_string", "blasst_last_error",
             "blasst_version")
 
@@ -113,6 +113,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.blasst_decode_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int,
                                                  ctypes.c_int, ctypes.c_int,
                                                  ctypes.POINTER(ctypes.c_size_t)]
+    lib.blasst_attn_decode_noalloc.restype = ctypes.c_int
+    lib.blasst_attn_decode_noalloc.argtypes = [vp, vp, vp, vp, u8p, fp, i64p, ctypes.POINTER(Shape),
+                                               ctypes.c_int, ctypes.c_int, ctypes.c_float,
+                                               ctypes.c_float, ctypes.c_int, vp]
     lib.blasst_attn_decode_workspace_size.restype = ctypes.c_size_t
     lib.blasst_attn_decode_workspace_size.argtypes = [ctypes.POINTER(Shape), ctypes.c_int,
                                                       ctypes.c_int]
@@ -391,6 +395,43 @@ def decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tenso
     return AttnResult(out, mask, lse, stats)
 
 
+def decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: Optional[torch.Tensor],
+                   lam: float, bc: int = 64, scale: Optional[float] = None,
+                   dv: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                   mask: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                   stats: Optional[torch.Tensor] = None,
+                   out_dtype: Optional[torch.dtype] = None) -> AttnResult:
+    """blasst_attn_decode_noalloc: the decode with the library's per-GPU static
+    scratch in place of a workspace. Outputs the caller passes are written in
+    place (nothing is allocated then); missing ones are allocated here with
+    torch.empty before the call, as in decode(). Calls on one GPU must not overlap."""
+    lib = load_library()
+    _require_device(q, k_cache, v_cache, out, mask, lse, stats)
+    B, Hq, d = q.shape
+    Hkv, Nk = k_cache.shape[1], k_cache.shape[2]
+    if v_cache is not None:
+        dv = v_cache.shape[3]
+    elif dv is None:
+        raise ValueError("dv is required for a latent cache")
+    dev = q.device
+    nkt = -(-Nk // bc)
+    if out is None:
+        out = torch.empty((B, Hq, dv), dtype=out_dtype or q.dtype, device=dev)
+    for t, shp, dt in ((mask, (B, Hq, nkt), torch.uint8), (lse, (B, Hq), torch.float32),
+                       (stats, (B, Hq, 3), torch.int64)):
+        if t is not None and (tuple(t.shape) != shp or t.dtype != dt or not t.is_contiguous()):
+            raise ValueError(f"output of shape {tuple(t.shape)} {t.dtype}: expected a contiguous "
+                             f"{shp} {dt}")
+    vs = _strides3(v_cache) if v_cache is not None else (0, 0, 0)
+    sh = Shape(B, Hq, Hkv, 1, Nk, d, dv, _strides3(q), _strides3(k_cache), vs, _strides3(out))
+    st = lib.blasst_attn_decode_noalloc(_ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(out),
+                                        _ptr(mask), _ptr(lse), _ptr(stats), ctypes.byref(sh),
+                                        _dtype_code(q.dtype), _dtype_code(out.dtype), float(lam),
+                                        float(scale) if scale else 0.0, int(bc), _stream(dev))
+    _check(st)
+    return AttnResult(out, mask, lse, stats)
+
+
 def decode_workspace_size(B: int, Hq: int, Hkv: int, Nk: int, d: int, dv: int,
                           latent: bool, dtype: torch.dtype = torch.bfloat16,
                           bc: int = 64) -> int:
@@ -417,5 +458,6 @@ def default_scale(d: int) -> float:
 
 
 __all__ = ["prefill", "prefill_masked", "prefill_backward", "quantize_mxfp4",
-           "prefill_twopass", "prefill_twopass_workspace_size", "decode", "decode_workspace_size", "load_library", "Shape", "BlasstError", "AttnResult",
+           "prefill_twopass", "prefill_twopass_workspace_size", "decode", "decode_noalloc",
+           "decode_workspace_size", "load_library", "Shape", "BlasstError", "AttnResult",
            "EXPORTED", "LIB_PATH", "STATUS"]

@@ -10,9 +10,18 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/blasst.h"
 #include "common.hpp"
+
+// Scratch of the allocation-free decode (blasst_attn_decode_noalloc): one
+// array per GPU, in the library's device code, alive until the process ends.
+// In host code `scratch` names a host-side stand-in, not device memory, so it is
+// never passed to a kernel or a copy: its device address on the current GPU
+// comes from hipGetSymbolAddress, once per device (scratch_address below), and
+// that address is what the kernels get.
+static __device__ __align__(256) char scratch[blasst::kNoAllocScratchBytes];
 
 namespace blasst {
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
@@ -293,6 +302,92 @@ size_t decode_workspace(const blasst_shape_t& s, DecodeKernel kind, int bc) {
                                             s.heads_q / s.heads_kv, nkt);
 }
 
+// Validates a decode call and fills its kernel arguments, the kernel kind and
+// the scratch bytes it needs; launches nothing.
+blasst_status_t prepare_decode(const void* q, const void* k_cache, const void* v_cache, void* out,
+                               uint8_t* mask_out, float* lse_out, int64_t* stats_out,
+                               const blasst_shape_t* shape, blasst_dtype_t dtype,
+                               blasst_dtype_t out_dtype, float lambda, float scale, int bc,
+                               blasst::DecodeArgs* args, DecodeKernel* kind_out, size_t* need) {
+  if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
+  if (missing(q, count(shape->batch, shape->heads_q, 1)) ||
+      missing(out, count(shape->batch, shape->heads_q, 1)) ||
+      missing(k_cache, count(shape->batch, shape->heads_kv, shape->len_kv)))
+    return fail(BLASST_E_NULL, "q, k_cache and out are required");
+  blasst_status_t st = check_dtypes(dtype, out_dtype);
+  if (st != BLASST_OK) return st;
+  const blasst_shape_t& s = *shape;
+  DecodeKernel kind;
+  st = check_decode(s, dtype, v_cache != nullptr, bc, &kind);
+  if (st != BLASST_OK) return st;
+  st = check_lambda_scale(lambda, scale);
+  if (st != BLASST_OK) return st;
+  const int elem = dtype == BLASST_FP32 ? 4 : 2;
+  const int oelem = out_dtype == BLASST_FP32 ? 4 : 2;
+  if (!aligned16(q) || !aligned16(k_cache) || (v_cache && !aligned16(v_cache)) || !aligned16(out))
+    return fail(BLASST_E_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
+  if (!strides_aligned(s.q_stride, 2, elem) || !strides_aligned(s.k_stride, 3, elem) ||
+      (v_cache && !strides_aligned(s.v_stride, 3, elem)) || !strides_aligned(s.o_stride, 2, oelem))
+    return fail(BLASST_E_ALIGN, "every stride times the element size must be a multiple of 16");
+  if (kind == DecodeKernel::kLatent && s.k_stride[2] < s.d_qk)
+    return fail(BLASST_E_SHAPE, "latent cache rows overlap (k_stride[2] = %lld < d_qk = %d)",
+                (long long)s.k_stride[2], s.d_qk);
+  if (kind == DecodeKernel::kLatent && s.k_stride[2] * 2 * 64 > (int64_t)INT32_MAX)
+    return fail(BLASST_E_UNSUPPORTED, "latent cache row stride too large (%lld elements)",
+                (long long)s.k_stride[2]);
+  const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)s.d_qk));
+  blasst::DecodeArgs a;
+  a.q = q; a.k = k_cache; a.v = v_cache; a.out = out;
+  a.mask = mask_out; a.lse = lse_out; a.stats = stats_out;
+  a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nk = s.len_kv;
+  a.G = s.heads_q / s.heads_kv;
+  a.nkt = (s.len_kv + bc - 1) / bc;
+  a.out_f32 = out_dtype == BLASST_FP32 ? 1 : 0;
+  a.qs0 = s.q_stride[0]; a.qs1 = s.q_stride[1];
+  a.ks0 = s.k_stride[0]; a.ks1 = s.k_stride[1]; a.ks2 = s.k_stride[2];
+  a.vs0 = s.v_stride[0]; a.vs1 = s.v_stride[1]; a.vs2 = s.v_stride[2];
+  a.os0 = s.o_stride[0]; a.os1 = s.o_stride[1];
+  a.scale = sc;
+  a.scale_log2 = sc * blasst::kLog2e;
+  a.thr_raw = raw_threshold(lambda, sc);
+  *args = a;
+  *kind_out = kind;
+  *need = decode_workspace(s, kind, bc);
+  return BLASST_OK;
+}
+
+blasst_status_t launch_decode(const blasst::DecodeArgs& a, DecodeKernel kind, void* workspace,
+                              hipStream_t hs) {
+  if (a.B == 0) return ok();
+  const hipError_t e = kind == DecodeKernel::kGqa ? blasst::launch_decode_gqa(a, hs)
+                                                  : blasst::launch_decode_mla(a, workspace, hs);
+  return hip_status(e, "decode launch");
+}
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+blasst_status_t scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(BLASST_E_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices)
+    return fail(BLASST_E_UNSUPPORTED, "device %d is beyond the %d devices the scratch table holds",
+                dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(BLASST_E_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return BLASST_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -328,33 +423,12 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
                                    blasst_dtype_t dtype, blasst_dtype_t out_dtype, float lambda,
                                    float scale, int bc, void* workspace, size_t workspace_bytes,
                                    void* stream) {
-  if (!shape) return fail(BLASST_E_NULL, "shape is NULL");
-  if (missing(q, count(shape->batch, shape->heads_q, 1)) ||
-      missing(out, count(shape->batch, shape->heads_q, 1)) ||
-      missing(k_cache, count(shape->batch, shape->heads_kv, shape->len_kv)))
-    return fail(BLASST_E_NULL, "q, k_cache and out are required");
-  blasst_status_t st = check_dtypes(dtype, out_dtype);
-  if (st != BLASST_OK) return st;
-  const blasst_shape_t& s = *shape;
+  blasst::DecodeArgs a;
   DecodeKernel kind;
-  st = check_decode(s, dtype, v_cache != nullptr, bc, &kind);
+  size_t need = 0;
+  blasst_status_t st = prepare_decode(q, k_cache, v_cache, out, mask_out, lse_out, stats_out, shape,
+                                      dtype, out_dtype, lambda, scale, bc, &a, &kind, &need);
   if (st != BLASST_OK) return st;
-  st = check_lambda_scale(lambda, scale);
-  if (st != BLASST_OK) return st;
-  const int elem = dtype == BLASST_FP32 ? 4 : 2;
-  const int oelem = out_dtype == BLASST_FP32 ? 4 : 2;
-  if (!aligned16(q) || !aligned16(k_cache) || (v_cache && !aligned16(v_cache)) || !aligned16(out))
-    return fail(BLASST_E_ALIGN, "q, k_cache, v_cache and out must be 16-byte aligned");
-  if (!strides_aligned(s.q_stride, 2, elem) || !strides_aligned(s.k_stride, 3, elem) ||
-      (v_cache && !strides_aligned(s.v_stride, 3, elem)) || !strides_aligned(s.o_stride, 2, oelem))
-    return fail(BLASST_E_ALIGN, "every stride times the element size must be a multiple of 16");
-  if (kind == DecodeKernel::kLatent && s.k_stride[2] < s.d_qk)
-    return fail(BLASST_E_SHAPE, "latent cache rows overlap (k_stride[2] = %lld < d_qk = %d)",
-                (long long)s.k_stride[2], s.d_qk);
-  if (kind == DecodeKernel::kLatent && s.k_stride[2] * 2 * 64 > (int64_t)INT32_MAX)
-    return fail(BLASST_E_UNSUPPORTED, "latent cache row stride too large (%lld elements)",
-                (long long)s.k_stride[2]);
-  const size_t need = decode_workspace(s, kind, bc);
   if (need > 0) {
     if (!workspace || workspace_bytes < need)
       return fail(BLASST_E_WORKSPACE, "workspace of %zu bytes needed (got %zu at %p)", need,
@@ -362,28 +436,32 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(BLASST_E_WORKSPACE, "workspace must be 256-byte aligned");
   }
+  return launch_decode(a, kind, workspace, reinterpret_cast<hipStream_t>(stream));
+}
 
-  const float sc = scale > 0.f ? scale : (float)(1.0 / std::sqrt((double)s.d_qk));
+blasst_status_t blasst_attn_decode_noalloc(const void* q, const void* k_cache,
+                                           const void* v_cache, void* out, uint8_t* mask_out,
+                                           float* lse_out, int64_t* stats_out,
+                                           const blasst_shape_t* shape, blasst_dtype_t dtype,
+                                           blasst_dtype_t out_dtype, float lambda, float scale,
+                                           int bc, void* stream) {
   blasst::DecodeArgs a;
-  a.q = q; a.k = k_cache; a.v = v_cache; a.out = out;
-  a.mask = mask_out; a.lse = lse_out; a.stats = stats_out;
-  a.B = s.batch; a.Hq = s.heads_q; a.Hkv = s.heads_kv; a.Nk = s.len_kv;
-  a.G = s.heads_q / s.heads_kv;
-  a.nkt = (s.len_kv + bc - 1) / bc;
-  a.out_f32 = out_dtype == BLASST_FP32 ? 1 : 0;
-  a.qs0 = s.q_stride[0]; a.qs1 = s.q_stride[1];
-  a.ks0 = s.k_stride[0]; a.ks1 = s.k_stride[1]; a.ks2 = s.k_stride[2];
-  a.vs0 = s.v_stride[0]; a.vs1 = s.v_stride[1]; a.vs2 = s.v_stride[2];
-  a.os0 = s.o_stride[0]; a.os1 = s.o_stride[1];
-  a.scale = sc;
-  a.scale_log2 = sc * blasst::kLog2e;
-  a.thr_raw = raw_threshold(lambda, sc);
-
-  hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
-  if (s.batch == 0) return ok();
-  const hipError_t e = kind == DecodeKernel::kGqa ? blasst::launch_decode_gqa(a, hs)
-                                                  : blasst::launch_decode_mla(a, workspace, hs);
-  return hip_status(e, "decode launch");
+  DecodeKernel kind;
+  size_t need = 0;
+  blasst_status_t st = prepare_decode(q, k_cache, v_cache, out, mask_out, lse_out, stats_out, shape,
+                                      dtype, out_dtype, lambda, scale, bc, &a, &kind, &need);
+  if (st != BLASST_OK) return st;
+  if (need > blasst::kNoAllocScratchBytes)
+    return fail(BLASST_E_UNSUPPORTED,
+                "this shape needs %zu bytes of scratch; the allocation-free decode holds %zu "
+                "(use blasst_attn_decode with a workspace)",
+                need, (size_t)blasst::kNoAllocScratchBytes);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_address(&ws);
+    if (st != BLASST_OK) return st;
+  }
+  return launch_decode(a, kind, ws, reinterpret_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

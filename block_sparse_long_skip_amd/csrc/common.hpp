@@ -20,6 +20,11 @@ constexpr float kNegInf = -__builtin_inff();
 // lists in LDS.
 constexpr int kPrefillMaxSetTiles = 6144;
 
+// Bytes of the per-GPU scratch array the allocation-free decode uses in place
+// of a caller's workspace (64 MiB: the batch-16 latent decode over 32768 keys
+// with 128 query heads needs about 37 MB).
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+
 // Arguments of every prefill kernel (element strides; last dim contiguous).
 struct PrefillArgs {
   const void* q;

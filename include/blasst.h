@@ -329,6 +329,27 @@ blasst_status_t blasst_attn_decode(const void* q, const void* k_cache, const voi
                                    void* stream);
 
 /*
+ * Allocation-free decode, for callers that cannot allocate device memory or
+ * take a workspace (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc). Same arguments, validation, kernels and
+ * results as blasst_attn_decode, without the workspace: the scratch the
+ * latent-cache decode needs (tile maxima, split partials) lives in one static
+ * device array per GPU inside the library, 64 MiB, reserved on each GPU the
+ * library runs on until the process ends. The call allocates nothing. A shape
+ * whose scratch (blasst_attn_decode_workspace_size) exceeds 64 MiB returns
+ * BLASST_E_UNSUPPORTED. Every call on one GPU uses that GPU's array: calls that
+ * overlap in time on one GPU (concurrent streams or host threads) race and
+ * must be serialised by the caller. Nothing in the array needs to start at any
+ * value; a call's contents are dead once it completes.
+ */
+blasst_status_t blasst_attn_decode_noalloc(const void* q, const void* k_cache,
+                                           const void* v_cache, void* out, uint8_t* mask_out,
+                                           float* lse_out, int64_t* stats_out,
+                                           const blasst_shape_t* shape, blasst_dtype_t dtype,
+                                           blasst_dtype_t out_dtype, float lambda, float scale,
+                                           int bc, void* stream);
+
+/*
  * Workspace bytes blasst_attn_decode needs for this shape, dtype, cache kind
  * (has_v_cache = 0 for a latent cache) and tile size; 0 when none is needed.
  * Validates like blasst_attn_decode (sizes, dtype, supported combination) and

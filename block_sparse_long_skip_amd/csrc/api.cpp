@@ -162,7 +162,8 @@ blasst_status_t prepare_prefill(const void* q, const void* k, const void* v, boo
     return fail(BLASST_E_UNSUPPORTED, "bf16 prefill needs key/value position strides <= 2^24 elements");
   const int64_t nqt = ((int64_t)s.len_q + br - 1) / br;
   const int64_t nkt = ((int64_t)s.len_kv + bc - 1) / bc;
-  if ((int64_t)s.batch * s.heads_q * nqt > 0x7fffffffLL)
+  // the bf16 kernel pads its grid to whole rounds of 8 (KV head, query tile) units
+  if ((int64_t)s.batch * s.heads_q * nqt + 8LL * (s.heads_q / s.heads_kv) > 0x7fffffffLL)
     return fail(BLASST_E_UNSUPPORTED, "grid too large");
   if (masked) {
     if (!b16)

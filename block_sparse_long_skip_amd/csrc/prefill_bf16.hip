@@ -96,15 +96,24 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  // block -> (query tile, head): heaviest query tiles first; when the head
-  // count is a multiple of 8, heads of one KV group land on the same XCD
-  // (blocks are dealt to the 8 XCDs round-robin)
-  const int nbh = a.B * a.Hq;
-  const int i = a.nqt - 1 - (int)(blockIdx.x / nbh);
-  int bh = (int)(blockIdx.x % nbh);
-  if ((nbh & 7) == 0) bh = (bh & 7) * (nbh >> 3) + (bh >> 3);
-  const int b = bh / a.Hq, hq = bh % a.Hq;
-  const int kvh = hq / (a.Hq / a.Hkv);
+  // block -> (query tile, batch, head). A unit of work is a (batch, KV head,
+  // query tile) triple; units go heaviest query tiles first. The G query heads
+  // of a unit read the same K/V tiles in the same order, so they take G
+  // consecutive slots of one XCD (the hardware deals blocks to the 8 XCDs
+  // round-robin: block x runs on XCD x % 8, as its slot x / 8 there) and run
+  // together out of that XCD's L2. Units are dealt to the XCDs round-robin;
+  // blocks past the last unit (when the unit count is not a multiple of 8)
+  // return at once.
+  const int G = a.Hq / a.Hkv;
+  const int ngrp = a.B * a.Hkv;
+  const int slot = (int)(blockIdx.x >> 3);
+  const int64_t u = (int64_t)(slot / G) * 8 + (blockIdx.x & 7);
+  if (u >= (int64_t)ngrp * a.nqt) return;
+  const int i = a.nqt - 1 - (int)(u / ngrp);
+  const int grp = (int)(u % ngrp);
+  const int b = grp / a.Hkv, kvh = grp % a.Hkv;
+  const int hq = kvh * G + slot % G;
+  const int bh = b * a.Hq + hq;
 
   const uint16_t* qp = (const uint16_t*)a.q + b * a.qs0 + hq * a.qs1;
   const char* kp = (const char*)((const uint16_t*)a.k + b * a.ks0 + kvh * a.ks1);
@@ -470,8 +479,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
 }
 
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
-  const int64_t nblocks = (int64_t)a.B * a.Hq * a.nqt;
-  if (nblocks == 0) return hipSuccess;
+  // whole rounds of 8 units (one per XCD), G blocks per unit
+  const int64_t units = (int64_t)a.B * a.Hkv * a.nqt;
+  const int64_t nblocks = (units + 7) / 8 * 8 * (a.Hq / a.Hkv);
+  if (units == 0) return hipSuccess;
   if (a.block_mask)
     hipLaunchKernelGGL(prefill_bf16_kernel<true>, dim3((unsigned)nblocks), dim3(NT), 0, stream, a);
   else

@@ -26,12 +26,13 @@ static __device__ __align__(256) char scratch[blasst::kNoAllocScratchBytes];
 namespace blasst {
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
-hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_gqa(const DecodeArgs& a, void* workspace, hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeArgs& a, void* workspace, hipStream_t stream);
 hipError_t launch_backward_bf16(const BackwardArgs& a, hipStream_t stream);
 hipError_t launch_mx_quantize_fp4(const MxQuantArgs& a, hipStream_t stream);
 hipError_t launch_twopass_map(const TwoPassMapArgs& a, hipStream_t stream);
 size_t decode_mla_workspace_bytes(int B, int Hq, int Hkv, int G, int nkt);
+size_t decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int G, int nkt);
 
 __global__ void zero_i64_kernel(int64_t* p, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -297,8 +298,11 @@ blasst_status_t check_decode(const blasst_shape_t& s, blasst_dtype_t dtype, bool
 }
 
 size_t decode_workspace(const blasst_shape_t& s, DecodeKernel kind, int bc) {
-  if (kind == DecodeKernel::kGqa || s.batch == 0) return 0;
+  if (s.batch == 0) return 0;
   const int nkt = (s.len_kv + bc - 1) / bc;
+  if (kind == DecodeKernel::kGqa)
+    return blasst::decode_gqa_workspace_bytes(s.batch, s.heads_q, s.heads_kv,
+                                              s.heads_q / s.heads_kv, nkt);
   return blasst::decode_mla_workspace_bytes(s.batch, s.heads_q, s.heads_kv,
                                             s.heads_q / s.heads_kv, nkt);
 }
@@ -360,7 +364,7 @@ blasst_status_t prepare_decode(const void* q, const void* k_cache, const void* v
 blasst_status_t launch_decode(const blasst::DecodeArgs& a, DecodeKernel kind, void* workspace,
                               hipStream_t hs) {
   if (a.B == 0) return ok();
-  const hipError_t e = kind == DecodeKernel::kGqa ? blasst::launch_decode_gqa(a, hs)
+  const hipError_t e = kind == DecodeKernel::kGqa ? blasst::launch_decode_gqa(a, workspace, hs)
                                                   : blasst::launch_decode_mla(a, workspace, hs);
   return hip_status(e, "decode launch");
 }

@@ -25,6 +25,20 @@
 //     output is deferred in the same order, so the arithmetic is unchanged.
 //   * Each wave keeps its own (m, l, O) partial; a log-sum-exp merge across
 //     the waves ends the kernel.
+//
+// Few sequences (batch x KV heads below half the CU count): one workgroup per
+// (batch, KV head) would leave most CUs idle, so the cache is split along its
+// length over workgroups, with exact decisions and no speculation:
+//   pass 1 (scores): each split computes S^T = K q^T for its tiles (the K
+//     bytes, read once) and stores the fp32 scores, every tile max and the
+//     split's maximum in the workspace (64 G floats per tile against the
+//     tile's 16 KB of K);
+//   pass 2 (accumulate): each split starts its running max from the maxima of
+//     the earlier splits, which is the exact prefix max at its first tile, and
+//     runs the same round loop on the stored scores: exact decisions, V read
+//     only for kept tiles, P.V, a log-sum-exp merge of its waves; its partial
+//     (m, l, O) goes to the workspace;
+//   merge: a log-sum-exp merge of the split partials of each (batch, head).
 #include "common.hpp"
 
 namespace blasst {
@@ -35,6 +49,7 @@ constexpr int D = 128;
 constexpr int NW = 4;
 constexpr int NT = NW * 64;
 constexpr int SLICE = BC * D * 2;  // 16 KB: one V tile, 64 rows x 256 B
+constexpr int kGqaSplitBlocks = 256;  // workgroups a split decode aims for
 
 
 // 16-byte chunk c of row r of a 64 x 256 B tile, chunk index XOR-swizzled by the row
@@ -43,7 +58,21 @@ __device__ __forceinline__ int vswz(int r, int c) {
 }
 }  // namespace
 
-__global__ void __launch_bounds__(NT, 1) decode_gqa_kernel(DecodeArgs a) {
+// Workspace of a split decode (carved from the caller's buffer).
+struct GqaSplit {
+  float* sc;       // [units][nkt][G][64]  scores (raw q.k units), lane order (kb, g, i)
+  float* smax;     // [units][nsplit][G]   maximum of each split's tile maxima
+  float* part_o;   // [B*Hq][nsplit][128]  the split's output (normalised by its l)
+  float* part_ml;  // [B*Hq][nsplit][2]    the split's (max, row sum); l = 0: nothing kept
+  int* part_kept;  // [B*Hq][nsplit]       kept tiles
+  int* part_vt;    // [units][nsplit]      V tiles read
+  int nsplit, T;
+};
+
+// MODE 0: the whole cache per workgroup; 1: split, scores only; 2: split,
+// exact decisions and accumulation on the stored scores
+template <int MODE>
+__global__ void __launch_bounds__(NT, 1) decode_gqa_kernel(DecodeArgs a, GqaSplit sp) {
   __shared__ __attribute__((aligned(16))) char Vs[NW][SLICE];
   __shared__ float tmx[2][NW][16];
   __shared__ int cnt[NW][17];
@@ -53,13 +82,19 @@ __global__ void __launch_bounds__(NT, 1) decode_gqa_kernel(DecodeArgs a) {
   const int w = t >> 6;
   const int n = lane & 15;  // head within the group (B/C operand column)
   const int g = lane >> 4;  // 0..3
-  const int bk = blockIdx.x;
-  const int b = bk / a.Hkv, kvh = bk % a.Hkv;
+  const int units = a.B * a.Hkv;
+  const int unit = MODE == 0 ? (int)blockIdx.x : (int)blockIdx.x % units;
+  const int split = MODE == 0 ? 0 : (int)blockIdx.x / units;
+  const int b = unit / a.Hkv, kvh = unit % a.Hkv;
   const int G = a.G;
   const bool hvalid = n < G;
   const int hq = kvh * G + n;
   const int nkt = a.nkt;
   const float c2 = a.scale_log2;
+  const int j0 = MODE == 0 ? 0 : split * sp.T;             // this workgroup's tiles
+  const int j1 = MODE == 0 ? nkt : min(j0 + sp.T, nkt);
+  // stored scores of (tile j, head n): 64 floats, this lane's 16 at (kb, g)
+  auto sc_at = [&](int j) { return sp.sc + (((int64_t)unit * nkt + j) * G + n) * 64 + 4 * g; };
 
   const uint16_t* qp = (const uint16_t*)a.q + b * a.qs0 + (int64_t)hq * a.qs1;
   const uint16_t* kp = (const uint16_t*)a.k + b * a.ks0 + kvh * a.ks1;
@@ -127,31 +162,55 @@ __global__ void __launch_bounds__(NT, 1) decode_gqa_kernel(DecodeArgs a) {
   float alpha_p = 1.f;
   bf16x8_t pb_p[2];
   u32x4_t vr[16];
-  const int nrounds = (nkt + NW - 1) / NW;
+  const int nrounds = (j1 - j0 + NW - 1) / NW;
+
+  if constexpr (MODE == 2) {
+    // the exact running max entering the split: the maxima of the earlier splits
+    if (hvalid)
+      for (int x = 0; x < split; ++x) Mg = fmaxf(Mg, sp.smax[((int64_t)unit * sp.nsplit + x) * G + n]);
+  }
+  float smx = kNegInf;  // pass 1: this lane's maximum over its tiles
 
   u32x4_t ka[4][D / 32], kn_[4][D / 32];
-  load_k(ka, min(w, nkt - 1));
+  if constexpr (MODE != 2) load_k(ka, min(j0 + w, j1 - 1));
+  // pass 2 reads the stored scores one round ahead instead of K
+  f32x4_t sa[4], sn_[4];
+  auto load_s = [&](f32x4_t (&sr)[4], int j) {
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      sr[kb] = hvalid ? *(const f32x4_t*)(sc_at(j) + 16 * kb) : (f32x4_t){0.f, 0.f, 0.f, 0.f};
+  };
+  if constexpr (MODE == 2) load_s(sa, min(j0 + w, j1 - 1));
 
   int r = 0;
-  // one round; kc holds this round's K tile, kn receives the next round's
-  auto round = [&](u32x4_t (&kc)[4][D / 32], u32x4_t (&kn)[4][D / 32]) {
-    const int j = r * NW + w;
-    const bool active = j < nkt;
+  // one round; kc / scs hold this round's K tile / stored scores, kn / snx
+  // receive the next round's
+  auto round = [&](u32x4_t (&kc)[4][D / 32], u32x4_t (&kn)[4][D / 32], f32x4_t (&scs)[4],
+                   f32x4_t (&snx)[4]) {
+    const int j = j0 + r * NW + w;
+    const bool active = j < j1;
     const int c0 = j * BC;
-    load_k(kn, min(j + NW, nkt - 1));  // every round, so the wait for kc stays precise
     f32x4_t s[4];
+    if constexpr (MODE != 2) {
+      load_k(kn, min(j + NW, j1 - 1));  // every round, so the wait for kc stays precise
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) {
-      s[kb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < 4; ++kb) {
+        s[kb] = (f32x4_t){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < D / 32; ++kk) s[kb] = mfma16x16x32(as_bf16x8(kc[kb][kk]), qb[kk], s[kb]);
-    }
-    if (c0 + BC > a.Nk) {
+        for (int kk = 0; kk < D / 32; ++kk)
+          s[kb] = mfma16x16x32(as_bf16x8(kc[kb][kk]), qb[kk], s[kb]);
+      }
+      if (c0 + BC > a.Nk) {
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (c0 + 16 * kb + 4 * g + i >= a.Nk) s[kb][i] = kNegInf;
+          for (int i = 0; i < 4; ++i)
+            if (c0 + 16 * kb + 4 * g + i >= a.Nk) s[kb][i] = kNegInf;
+      }
+    } else {
+      load_s(snx, min(j + NW, j1 - 1));
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) s[kb] = scs[kb];
     }
     float tm = kNegInf;
     if (active) {
@@ -160,6 +219,16 @@ __global__ void __launch_bounds__(NT, 1) decode_gqa_kernel(DecodeArgs a) {
         tm = fmaxf(tm, fmaxf(fmaxf(s[kb][0], s[kb][1]), fmaxf(s[kb][2], s[kb][3])));
       tm = fmaxf(tm, shfl_xor_f(tm, 16));
       tm = fmaxf(tm, shfl_xor_f(tm, 32));
+    }
+    if constexpr (MODE == 1) {
+      // scores only: store this tile's scores, keep the split's maximum
+      if (active && hvalid) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) *(f32x4_t*)(sc_at(j) + 16 * kb) = s[kb];
+        smx = fmaxf(smx, tm);
+      }
+      ++r;
+      return;
     }
     if (g == 0) tmx[r & 1][w][n] = tm;
     __syncthreads();
@@ -225,9 +294,18 @@ __global__ void __launch_bounds__(NT, 1) decode_gqa_kernel(DecodeArgs a) {
     ++r;
   };
   while (r < nrounds) {
-    round(ka, kn_);
+    round(ka, kn_, sa, sn_);
     if (r >= nrounds) break;
-    round(kn_, ka);
+    round(kn_, ka, sn_, sa);
+  }
+  if constexpr (MODE == 1) {
+    // the split's maximum per head: over the lanes of a head, then the waves
+    if (g == 0) tmx[0][w][n] = smx;
+    __syncthreads();
+    if (w == 0 && g == 0 && hvalid)
+      sp.smax[((int64_t)unit * sp.nsplit + split) * G + n] =
+          fmaxf(fmaxf(tmx[0][0][n], tmx[0][1][n]), fmaxf(tmx[0][2][n], tmx[0][3][n]));
+    return;
   }
   if (pend) {
 #pragma unroll
@@ -259,14 +337,29 @@ __global__ void __launch_bounds__(NT, 1) decode_gqa_kernel(DecodeArgs a) {
 #pragma unroll
     for (int x = 0; x < NW; ++x) M = fmaxf(M, reinterpret_cast<const float*>(Vs[x])[D * 16 + hn]);
     float L = 0.f, acc = 0.f;
+    if (M != kNegInf) {  // (a split may keep nothing for a head)
 #pragma unroll
-    for (int x = 0; x < NW; ++x) {
-      const float* px = reinterpret_cast<const float*>(Vs[x]);
-      const float wgt = fast_exp2((px[D * 16 + hn] - M) * c2);
-      L += px[D * 16 + 16 + hn] * wgt;
-      acc += px[dv * 16 + hn] * wgt;
+      for (int x = 0; x < NW; ++x) {
+        const float* px = reinterpret_cast<const float*>(Vs[x]);
+        const float wgt = fast_exp2((px[D * 16 + hn] - M) * c2);
+        L += px[D * 16 + 16 + hn] * wgt;
+        acc += px[dv * 16 + hn] * wgt;
+      }
     }
     const int hh = kvh * G + hn;
+    if constexpr (MODE == 2) {
+      const int64_t prow = ((int64_t)b * a.Hq + hh) * sp.nsplit + split;
+      sp.part_o[prow * D + dv] = L > 0.f ? acc / L : 0.f;
+      if (dv == 0) {
+        sp.part_ml[2 * prow] = M;
+        sp.part_ml[2 * prow + 1] = L;
+        int kt = 0, vl = 0;
+        for (int x = 0; x < NW; ++x) { kt += cnt[x][hn]; vl += cnt[x][16]; }
+        sp.part_kept[prow] = kt;
+        if (hn == 0) sp.part_vt[(int64_t)unit * sp.nsplit + split] = vl;
+      }
+      continue;
+    }
     store_out1(a.out, b * a.os0 + (int64_t)hh * a.os1 + dv, a.out_f32, acc / L);
     if (dv == 0) {
       if (a.lse) a.lse[(int64_t)b * a.Hq + hh] = M * a.scale + logf(L);
@@ -282,10 +375,130 @@ __global__ void __launch_bounds__(NT, 1) decode_gqa_kernel(DecodeArgs a) {
   }
 }
 
-hipError_t launch_decode_gqa(const DecodeArgs& a, hipStream_t stream) {
-  const int64_t nblocks = (int64_t)a.B * a.Hkv;
-  if (nblocks == 0) return hipSuccess;
-  hipLaunchKernelGGL(decode_gqa_kernel, dim3((unsigned)nblocks), dim3(NT), 0, stream, a);
+// Log-sum-exp merge of the split partials of one (batch, head) per wave, and
+// the statistics. 4 rows per block; lane l owns features 2l and 2l + 1.
+__global__ void __launch_bounds__(256) decode_gqa_merge_kernel(DecodeArgs a, GqaSplit sp) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= (int64_t)a.B * a.Hq) return;
+  const int b = (int)(row / a.Hq), hq = (int)(row % a.Hq);
+  const int unit = b * a.Hkv + hq / a.G;
+  const float c2 = a.scale_log2;
+  const float* ml = sp.part_ml + row * sp.nsplit * 2;
+  float ms = kNegInf;
+  for (int x = 0; x < sp.nsplit; ++x)
+    if (ml[2 * x + 1] > 0.f) ms = fmaxf(ms, ml[2 * x]);
+  float L = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int x = 0; x < sp.nsplit; ++x) {
+    const float l = ml[2 * x + 1];
+    if (!(l > 0.f)) continue;
+    const float wl = l * fast_exp2((ml[2 * x] - ms) * c2);
+    const float* po = sp.part_o + (row * sp.nsplit + x) * D + 2 * lane;
+    L += wl;
+    o0 += po[0] * wl;
+    o1 += po[1] * wl;
+  }
+  const int64_t ob = b * a.os0 + (int64_t)hq * a.os1 + 2 * lane;
+  store_out1(a.out, ob, a.out_f32, o0 / L);
+  store_out1(a.out, ob + 1, a.out_f32, o1 / L);
+  if (a.lse && lane == 0) a.lse[row] = ms * a.scale + logf(L);
+  if (a.stats) {
+    int kept = 0, vt = 0;
+    for (int x = lane; x < sp.nsplit; x += 64) {
+      kept += sp.part_kept[row * sp.nsplit + x];
+      vt += sp.part_vt[(int64_t)unit * sp.nsplit + x];
+    }
+    for (int d = 32; d >= 1; d >>= 1) {
+      kept += __shfl_xor(kept, d, 64);
+      vt += __shfl_xor(vt, d, 64);
+    }
+    if (lane == 0) {
+      int64_t* st = a.stats + row * 3;
+      st[0] = a.nkt;
+      st[1] = kept;
+      st[2] = vt;
+    }
+  }
+}
+
+namespace {
+struct GqaPlan {
+  int nsplit, T;  // nsplit = 1: one workgroup per (batch, KV head), no workspace
+  size_t off_sc, off_smax, off_o, off_ml, off_kept, off_vt, bytes;
+};
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Split the cache when the (batch, KV head) pairs fill less than half of the
+// 256 CUs: about one workgroup per CU in total, whole rounds of 4 tiles per
+// split.
+GqaPlan gqa_plan(int B, int Hq, int Hkv, int G, int nkt) {
+  GqaPlan p{};
+  const int64_t units = (int64_t)B * Hkv;
+  p.nsplit = 1;
+  p.T = nkt;
+  if (units > 0 && units < 128) {
+    const int64_t want = (kGqaSplitBlocks + units - 1) / units;
+    int T = (int)((nkt + want - 1) / want);
+    T = (T + NW - 1) / NW * NW;
+    const int ns = (nkt + T - 1) / T;
+    if (ns > 1) {
+      p.nsplit = ns;
+      p.T = T;
+    }
+  }
+  if (p.nsplit == 1) return p;
+  const size_t rows = (size_t)B * Hq;
+  size_t off = 0;
+  p.off_sc = off;
+  off = align256(off + (size_t)units * nkt * G * 64 * sizeof(float));
+  p.off_smax = off;
+  off = align256(off + (size_t)units * p.nsplit * G * sizeof(float));
+  p.off_o = off;
+  off = align256(off + rows * p.nsplit * D * sizeof(float));
+  p.off_ml = off;
+  off = align256(off + rows * p.nsplit * 2 * sizeof(float));
+  p.off_kept = off;
+  off = align256(off + rows * p.nsplit * sizeof(int));
+  p.off_vt = off;
+  off = align256(off + (size_t)units * p.nsplit * sizeof(int));
+  p.bytes = off;
+  return p;
+}
+}  // namespace
+
+size_t decode_gqa_workspace_bytes(int B, int Hq, int Hkv, int G, int nkt) {
+  return gqa_plan(B, Hq, Hkv, G, nkt).bytes;
+}
+
+hipError_t launch_decode_gqa(const DecodeArgs& a, void* workspace, hipStream_t stream) {
+  const int64_t units = (int64_t)a.B * a.Hkv;
+  if (units == 0) return hipSuccess;
+  const GqaPlan p = gqa_plan(a.B, a.Hq, a.Hkv, a.G, a.nkt);
+  GqaSplit sp{};
+  sp.nsplit = p.nsplit;
+  sp.T = p.T;
+  if (p.nsplit == 1) {
+    hipLaunchKernelGGL(decode_gqa_kernel<0>, dim3((unsigned)units), dim3(NT), 0, stream, a, sp);
+    return hipGetLastError();
+  }
+  char* base = static_cast<char*>(workspace);
+  sp.sc = reinterpret_cast<float*>(base + p.off_sc);
+  sp.smax = reinterpret_cast<float*>(base + p.off_smax);
+  sp.part_o = reinterpret_cast<float*>(base + p.off_o);
+  sp.part_ml = reinterpret_cast<float*>(base + p.off_ml);
+  sp.part_kept = reinterpret_cast<int*>(base + p.off_kept);
+  sp.part_vt = reinterpret_cast<int*>(base + p.off_vt);
+  const unsigned nb = (unsigned)(units * p.nsplit);
+  hipLaunchKernelGGL(decode_gqa_kernel<1>, dim3(nb), dim3(NT), 0, stream, a, sp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_gqa_kernel<2>, dim3(nb), dim3(NT), 0, stream, a, sp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t rows = (int64_t)a.B * a.Hq;
+  hipLaunchKernelGGL(decode_gqa_merge_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                     stream, a, sp);
   return hipGetLastError();
 }
 

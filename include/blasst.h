@@ -313,8 +313,14 @@ blasst_status_t blasst_prefill_backward_workspace_size(const blasst_shape_t* sha
  *             is 0. Calls that overlap in time must not share a workspace.
  *
  * Supported (else BLASST_E_UNSUPPORTED), all BLASST_BF16 inputs with bc = 64:
- *   d_qk = d_v = 128 with a separate v_cache, heads_q / heads_kv <= 16
- *           (no workspace);
+ *   d_qk = d_v = 128 with a separate v_cache, heads_q / heads_kv <= 16.
+ *           With batch * heads_kv >= 128 one workgroup walks each cache (no
+ *           workspace). Below that the cache is split along its length over
+ *           workgroups: a first pass stores the scores and tile maxima in the
+ *           workspace, a second decides exactly from them, reads V for kept
+ *           tiles only and writes per-split partials, and a log-sum-exp merge
+ *           ends the call; the workspace grows with
+ *           batch * heads_kv * ceil(Nk/64) * 256 * (heads_q/heads_kv) bytes;
  *   d_qk = 576, d_v = 512, v_cache NULL (latent cache), any heads_q / heads_kv.
  *           The cache is split along its length over workgroups; the
  *           workspace holds the tile maxima, the per-split partial outputs

@@ -372,10 +372,17 @@ def test_decode_validation(case, expect):
 
 
 def test_decode_workspace_size():
-    """GQA decode needs no workspace; a latent cache needs one that grows with
-    the cache length and the batch, and the query validates like the call."""
-    st, n = _ws_size(_shape(Hq=8, Hkv=2, Nq=1, Nk=1000), True)
+    """GQA decode over enough (batch, KV head) pairs needs no workspace; fewer
+    pairs split the cache and need one for the scores, maxima and partials; a
+    latent cache needs one that grows with the cache length and the batch, and
+    the query validates like the call."""
+    st, n = _ws_size(_shape(B=32, Hq=32, Hkv=8, Nq=1, Nk=65536), True)
     assert (st, n) == (0, 0)
+    st, n = _ws_size(_shape(B=1, Hq=32, Hkv=8, Nq=1, Nk=65536), True)
+    # at least the stored scores: 64 floats per (KV head, tile, query head)
+    assert st == 0 and n >= 8 * 1024 * 4 * 64 * 4 and n % 256 == 0
+    st, n = _ws_size(_shape(Hq=8, Hkv=2, Nq=1, Nk=64), True)
+    assert (st, n) == (0, 0)  # a single tile: nothing to split
     sizes = []
     for B, Nk in [(1, 1000), (1, 64000), (4, 64000)]:
         st, n = _ws_size(_shape(B=B, Hq=128, Hkv=1, Nq=1, Nk=Nk, d=576, dv=512), False)
@@ -400,6 +407,7 @@ def test_attn_decode_workspace_size_contract_form():
     lib = A.load_library()
     size_max = ctypes.c_size_t(-1).value
     for sh, has_v in [(_shape(Hq=8, Hkv=2, Nq=1, Nk=1000), True),
+                      (_shape(B=32, Hq=32, Hkv=8, Nq=1, Nk=4096), True),
                       (_shape(B=3, Hq=128, Hkv=1, Nq=1, Nk=9000, d=576, dv=512), False),
                       (_shape(B=1, Hq=20, Hkv=2, Nq=1, Nk=300, d=576, dv=512), False)]:
         st, n = _ws_size(sh, has_v)

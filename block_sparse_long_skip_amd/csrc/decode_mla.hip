@@ -189,10 +189,10 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
   // counts, and whether pass 0 took the same decisions
   float m_init = kNegInf;
   // pass 0 of a split after the first scores tile 0 (which holds the attention
-  // sinks) before its own tiles: its maxima start the split's running max, a
-  // lower bound of the exact one that usually equals it, so the speculative
-  // decisions usually are the exact ones
-  const int pre = (MODE == 0 && s > 0) ? 1 : 0;
+  // sinks) before its own tiles when tiles can be dropped at all: its maxima
+  // start the split's running max, a lower bound of the exact one that usually
+  // equals it, so the speculative decisions usually are the exact ones
+  const int pre = (MODE == 0 && s > 0 && thr != kNegInf) ? 1 : 0;
   int nl = j1 - j0 + pre;
   if constexpr (MODE == 1) {
     const int tn = j1 - j0;

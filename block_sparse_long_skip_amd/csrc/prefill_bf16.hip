@@ -354,7 +354,10 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
       // max has grown by more than 2^8 (any lane of the wave), or on the first tile
       const bool grow = (st.m_prefix - st.m_acc) * c2 > kLazyRescaleLog2;
       if (__any(grow)) {
-        const float alpha = fast_exp2((st.m_acc - st.m_prefix) * c2);
+        // a row that has seen no key yet (block-sparse mode: its running max is
+        // still -inf) keeps its empty sums as they are
+        const float alpha =
+            st.m_prefix == kNegInf ? 1.f : fast_exp2((st.m_acc - st.m_prefix) * c2);
         st.m_acc = st.m_prefix;
         st.l *= alpha;
 #pragma unroll
@@ -363,7 +366,8 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
           for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       }
     }
-    const float mc = st.m_acc * c2;
+    // (a row with no reference max yet has only -inf scores: p = 0 against 0)
+    const float mc = st.m_acc == kNegInf ? 0.f : st.m_acc * c2;
     if (has_next && keep) {
       scores_and_probs(Ks[P ^ 1], sn, s, mc, pb, st.l);
     } else if (has_next) {

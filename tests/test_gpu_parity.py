@@ -223,6 +223,19 @@ def test_decode_gqa_b32_n65536(lam, gain, out):
         assert res.skip_fraction > 0.3
 
 
+@pytest.mark.parametrize("lam,gain", [(0.0, 1.0), (1e-3, 1.0), (1e-3, 6.0), (1e-2, 6.0)])
+def test_decode_gqa_b1_n65536_split(lam, gain):
+    """One sequence with 8 KV heads fills 8 of the 256 CUs with one workgroup
+    per (batch, KV head), so the cache is split along its length: scores and
+    tile maxima first, then exact decisions and P.V per split, then a
+    log-sum-exp merge. Every (KV head, query head) row against the oracle."""
+    w = synth.WORKLOADS[3].scaled(B=1).with_gain(gain)
+    assert A.decode_workspace_size(w.B, w.Hq, w.Hkv, w.Nk, w.d, w.dv, latent=False) > 0
+    res = _check_decode(w, lam, out="fp32")
+    if gain > 1 and lam > 0:
+        assert res.skip_fraction > 0.3
+
+
 # The latent-cache kernel splits the cache over workgroups (one split per
 # tile at these sizes, a few tiles per split at the larger ones) and redoes the
 # splits whose speculative decisions differ from the exact ones; two head
@@ -414,6 +427,26 @@ def test_prefill_masked_edge_sets(out):
     last[..., nkt - 1] = 1  # causal: only the last query rows reach it
     _check_masked_full(w, last, 1e-2, f"masked last-tile-only out={out}", out)
     _check_masked_full(w.scaled(causal=False), last, 1e-2, f"masked tail non-causal out={out}", out)
+
+
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_prefill_masked_first_tile_is_the_diagonal(out):
+    """Each query tile's set holds only the key tile of its last row's causal
+    limit, with Nk - Nq = 133 (not a multiple of 32): inside a wave, rows whose
+    limit falls before that tile see nothing while the others start their
+    running max there, so one wave mixes rows that rescale with rows that have
+    no reference max (they must come out as zeros with lse -inf)."""
+    w = synth.small_workload("prefill", B=1, Hq=2, Hkv=1, Nq=200, Nk=333, seed=47, gain=6.0,
+                             window=32)
+    nqt, nkt = synth.n_tiles(w.Nq, w.br), synth.n_tiles(w.Nk, w.bc)
+    sel = np.zeros((1, 2, nqt, nkt), np.uint8)
+    for i in range(nqt):
+        last = min((i + 1) * w.br, w.Nq) - 1
+        sel[..., i, (last + w.Nk - w.Nq) // w.bc] = 1
+    res = _check_masked_full(w, sel, 1e-2, f"masked diagonal-first out={out}", out)
+    lse = res.lse.cpu().numpy()
+    assert np.isneginf(lse).any() and np.isfinite(lse).any()
+    assert torch.isfinite(res.out.float()).all()
 
 
 def test_prefill_masked_full_set_matches_prefill():

@@ -42,7 +42,8 @@ already resident in HBM. The line printed on stdout carries:
                pre-pass, then exact attention over the kept tiles): time against
                the one-pass call, the pre-pass share, agreement of its map with
                the exact rule's mask, and FP4 TFLOP/s of the pre-pass
-  decode       the batch-32 GQA decode over 65536 keys and the batch-16 MLA
+  decode       the batch-32 GQA decode over 65536 keys, the same layer for one
+               sequence (cache split over workgroups) and the batch-16 MLA
                decode over 32768 latent keys: GB/s of the bytes actually read
                (K always, V only for tiles some head keeps) against 8 TB/s
   cpu_baseline the CPU oracle timed on a bounded sample of query tiles of the
@@ -96,7 +97,7 @@ def parse():
     ap.add_argument("--no-twopass", action="store_true", help="skip the two-pass prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
     ap.add_argument("--only", choices=["prefill", "prefill_masked", "backward", "twopass", "decode_gqa",
-                                       "decode_mla", "copy"],
+                                       "decode_gqa_b1", "decode_mla", "copy"],
                     help="launch only this kernel --steps times (for rocprofv3 counter passes)")
     ap.add_argument("--workload", choices=["qwen7b", "llama8b"], default="qwen7b",
                     help="prefill layer of --only prefill: the 131072-long Qwen2.5-7B shape or "
@@ -451,8 +452,11 @@ def bench_decode(args):
 
     results = {}
     flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB, evicts L2 and MALL
-    for cid, kind in ((3, "decode_gqa_b32_n65536"), (5, "decode_mla_b16_n32768")):
-        w = synth.WORKLOADS[cid]
+    # the batch-32 GQA decode, the same layer for a single sequence (its cache
+    # split over workgroups), and the batch-16 MLA decode
+    for w, kind in ((synth.WORKLOADS[3], "decode_gqa_b32_n65536"),
+                    (synth.WORKLOADS[3].scaled(B=1), "decode_gqa_b1_n65536"),
+                    (synth.WORKLOADS[5], "decode_mla_b16_n32768")):
         rows = []
         for gain in (1.0, 6.0):
             log(f"[bench] generating {w.name} gain {gain}")
@@ -575,8 +579,10 @@ def only(args):
         log(f"[bench] launched backward x {args.steps}")
         return
     cid = {"prefill": {"qwen7b": 4, "llama8b": 2}[args.workload], "prefill_masked": 2,
-           "decode_gqa": 3, "decode_mla": 5}[args.only]
+           "decode_gqa": 3, "decode_gqa_b1": 3, "decode_mla": 5}[args.only]
     w = synth.WORKLOADS[cid]
+    if args.only == "decode_gqa_b1":
+        w = w.scaled(B=1)  # one sequence: the cache is split over workgroups
     inp = synth.make_inputs(w)
     q, k = to_device(inp.q, w), to_device(inp.k, w)
     v = to_device(inp.v, w) if inp.v is not None else None

@@ -125,14 +125,20 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  // block -> (query tile, head), as in the bf16 prefill: heaviest query tiles
-  // first, heads of one KV group on one XCD when the head count allows
-  const int nbh = a.B * a.Hq;
-  const int i = a.nqt - 1 - (int)(blockIdx.x / nbh);
-  int bh = (int)(blockIdx.x % nbh);
-  if ((nbh & 7) == 0) bh = (bh & 7) * (nbh >> 3) + (bh >> 3);
-  const int b = bh / a.Hq, hq = bh % a.Hq;
-  const int kvh = hq / (a.Hq / a.Hkv);
+  // block -> (query tile, batch, head), as in the bf16 prefill: units of one
+  // (batch, KV head, query tile), heaviest query tiles first, the G query heads
+  // of a unit in G consecutive slots of one XCD (block x runs on XCD x % 8, as
+  // its slot x / 8 there); blocks past the last unit return at once
+  const int G = a.Hq / a.Hkv;
+  const int ngrp = a.B * a.Hkv;
+  const int slot = (int)(blockIdx.x >> 3);
+  const int64_t u = (int64_t)(slot / G) * 8 + (blockIdx.x & 7);
+  if (u >= (int64_t)ngrp * a.nqt) return;
+  const int i = a.nqt - 1 - (int)(u / ngrp);
+  const int grp = (int)(u % ngrp);
+  const int b = grp / a.Hkv, kvh = grp % a.Hkv;
+  const int hq = kvh * G + slot % G;
+  const int bh = b * a.Hq + hq;
 
   const int row = i * BR + 32 * w + l32;
   const bool valid = row < a.Nq;
@@ -284,8 +290,10 @@ hipError_t launch_mx_quantize_fp4(const MxQuantArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_twopass_map(const TwoPassMapArgs& a, hipStream_t stream) {
-  const int64_t nblocks = (int64_t)a.B * a.Hq * a.nqt;
-  if (nblocks == 0) return hipSuccess;
+  // whole rounds of 8 units (one per XCD), G blocks per unit
+  const int64_t units = (int64_t)a.B * a.Hkv * a.nqt;
+  const int64_t nblocks = (units + 7) / 8 * 8 * (a.Hq / a.Hkv);
+  if (units == 0) return hipSuccess;
   hipLaunchKernelGGL(twopass_map_kernel, dim3((unsigned)nblocks), dim3(NT), 0, stream, a);
   return hipGetLastError();
 }

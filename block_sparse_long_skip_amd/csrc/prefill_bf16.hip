@@ -186,23 +186,25 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
   }
 
   // S^T for one key tile from LDS: the two 32-key blocks are independent MFMA
-  // chains, interleaved, with each step's two K operands read one step ahead
+  // chains, interleaved, with each step's two K operands read two steps ahead
+  // (a three-deep register ring) so the LDS latency is covered by four MFMAs
   auto scores = [&](const char* kt, f32x16_t (&s)[2]) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[0][r] = s[1][r] = 0.f;
-    u32x4_t cur0 = *(const u32x4_t*)(kt + kro[0]);
-    u32x4_t cur1 = *(const u32x4_t*)(kt + 8192 + kro[0]);
+    u32x4_t ka[3], kb[3];
+    ka[0] = *(const u32x4_t*)(kt + kro[0]);
+    kb[0] = *(const u32x4_t*)(kt + 8192 + kro[0]);
+    ka[1] = *(const u32x4_t*)(kt + kro[1]);
+    kb[1] = *(const u32x4_t*)(kt + 8192 + kro[1]);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4_t nx0 = cur0, nx1 = cur1;
-      if (kk + 1 < D / 16) {
-        nx0 = *(const u32x4_t*)(kt + kro[kk + 1]);
-        nx1 = *(const u32x4_t*)(kt + 8192 + kro[kk + 1]);
+      if (kk + 2 < D / 16) {
+        ka[(kk + 2) % 3] = *(const u32x4_t*)(kt + kro[kk + 2]);
+        kb[(kk + 2) % 3] = *(const u32x4_t*)(kt + 8192 + kro[kk + 2]);
       }
-      s[0] = mfma32x32x16(as_bf16x8(cur0), qb[kk], s[0]);
-      s[1] = mfma32x32x16(as_bf16x8(cur1), qb[kk], s[1]);
-      cur0 = nx0;
-      cur1 = nx1;
+      s[0] = mfma32x32x16(as_bf16x8(ka[kk % 3]), qb[kk], s[0]);
+      s[1] = mfma32x32x16(as_bf16x8(kb[kk % 3]), qb[kk], s[1]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   // P_j (bf16, B-operand layout of chunk c: keys 16c + 8(e/4) + 4h + e%4)
@@ -221,32 +223,33 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
     ls1 += p1 + p3;
   };
   // S_{j+1} on MFMA and P_j on the VALU, interleaved in program order: each of
-  // the 8 steps issues the next step's two K-operand reads, two MFMAs (one per
-  // 32-key block) and a quarter-chunk of P_j; the scheduling fence keeps that
-  // order, so a wave fills its own MFMA dependency stalls with softmax work
+  // the 8 steps issues the two K-operand reads of the step after next, two
+  // MFMAs (one per 32-key block) and a quarter-chunk of P_j; the scheduling
+  // fence keeps that order, so a wave fills its own MFMA dependency stalls
+  // with softmax work
   auto scores_and_probs = [&](const char* kt, f32x16_t (&sn)[2], const f32x16_t (&s)[2],
                               float mc, bf16x8_t (&pb)[4], float& lsum) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) sn[0][r] = sn[1][r] = 0.f;
     uint32_t pw[4][4];
     float ls0 = 0.f, ls1 = 0.f;
-    u32x4_t cur0 = *(const u32x4_t*)(kt + kro[0]);
-    u32x4_t cur1 = *(const u32x4_t*)(kt + 8192 + kro[0]);
+    u32x4_t ka[3], kb[3];
+    ka[0] = *(const u32x4_t*)(kt + kro[0]);
+    kb[0] = *(const u32x4_t*)(kt + 8192 + kro[0]);
+    ka[1] = *(const u32x4_t*)(kt + kro[1]);
+    kb[1] = *(const u32x4_t*)(kt + 8192 + kro[1]);
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      u32x4_t nx0 = cur0, nx1 = cur1;
-      if (kk + 1 < D / 16) {
-        nx0 = *(const u32x4_t*)(kt + kro[kk + 1]);
-        nx1 = *(const u32x4_t*)(kt + 8192 + kro[kk + 1]);
+      if (kk + 2 < D / 16) {
+        ka[(kk + 2) % 3] = *(const u32x4_t*)(kt + kro[kk + 2]);
+        kb[(kk + 2) % 3] = *(const u32x4_t*)(kt + 8192 + kro[kk + 2]);
       }
-      sn[0] = mfma32x32x16(as_bf16x8(cur0), qb[kk], sn[0]);
-      sn[1] = mfma32x32x16(as_bf16x8(cur1), qb[kk], sn[1]);
+      sn[0] = mfma32x32x16(as_bf16x8(ka[kk % 3]), qb[kk], sn[0]);
+      sn[1] = mfma32x32x16(as_bf16x8(kb[kk % 3]), qb[kk], sn[1]);
       probs_step(s, mc, kk, pw, ls0, ls1);
       // consume this step's results here so they are not sunk past the MFMAs
       asm volatile("" ::"v"(pw[kk >> 1][2 * (kk & 1)]), "v"(pw[kk >> 1][2 * (kk & 1) + 1]),
                    "v"(ls0), "v"(ls1));
-      cur0 = nx0;
-      cur1 = nx1;
       __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
@@ -426,6 +429,16 @@ __global__ void __launch_bounds__(NT, 2) prefill_bf16_kernel(PrefillArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) va[db] = vb[db];
       }
+      // schedule: the first three MFMAs' V^T reads, then each MFMA followed by
+      // the reads of the MFMA three places later (left alone, the scheduler
+      // issues each read pair just one MFMA ahead of its use)
+      __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+      for (int x = 0; x < 13; ++x) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0);
       ++kept;
     }
     keep = keep_next;

@@ -101,8 +101,15 @@ __global__ void __launch_bounds__(NT) bwd_delta_kernel(BackwardArgs a) {
 
 // ---------------------------------------------------------------------------
 __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(BackwardArgs a) {
-  // KV[0], KV[1]: K tiles of the two buffers; KV[2], KV[3]: the matching V tiles
-  __shared__ __attribute__((aligned(16))) char KV[4][KTILE];
+  // K and V tiles of the two buffers, each its own LDS array: the compiler
+  // tracks copies into LDS per array, so a read of one buffer does not wait
+  // for the copy in flight into the other
+  __shared__ __attribute__((aligned(16))) char K0[KTILE];
+  __shared__ __attribute__((aligned(16))) char K1[KTILE];
+  __shared__ __attribute__((aligned(16))) char V0[KTILE];
+  __shared__ __attribute__((aligned(16))) char V1[KTILE];
+  char* const Ks[2] = {K0, K1};
+  char* const Vs[2] = {V0, V1};
   __shared__ uint16_t tlist[kBackwardMaxTiles];
   __shared__ int wcount[4];
 
@@ -224,17 +231,27 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(BackwardArgs a) {
     tro[db][1] = swz(r0 + 8, dv0 >> 3) + ((dv0 & 7) << 1);
   }
 
-  // X^T[32 keys][32 rows] = T Y^T for the 32-key half of a key tile at kt (LDS)
-  // and Y^T in registers; the two products share the operand reads' order
-  auto scores2 = [&](const char* kt, f32x16_t& s, f32x16_t& dp) __attribute__((always_inline)) {
+  // S^T = K Q^T and dP^T = V dO^T for the 32-key half of a key tile (K at kt,
+  // V at vt in LDS; Q^T, dO^T in registers); each step's two operands are read
+  // two steps ahead (a three-deep register ring)
+  auto scores2 = [&](const char* kt, const char* vt, f32x16_t& s, f32x16_t& dp)
+      __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+    u32x4_t xk[3], xv[3];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      xk[kk] = *(const u32x4_t*)(kt + kro[kk]);
+      xv[kk] = *(const u32x4_t*)(vt + kro[kk]);
+    }
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      const u32x4_t xk = *(const u32x4_t*)(kt + kro[kk]);
-      const u32x4_t xv = *(const u32x4_t*)(kt + 2 * KTILE + kro[kk]);
-      s = mfma32x32x16(as_bf16x8(xk), qb[kk], s);
-      dp = mfma32x32x16(as_bf16x8(xv), gb[kk], dp);
+      if (kk + 2 < D / 16) {
+        xk[(kk + 2) % 3] = *(const u32x4_t*)(kt + kro[kk + 2]);
+        xv[(kk + 2) % 3] = *(const u32x4_t*)(vt + kro[kk + 2]);
+      }
+      s = mfma32x32x16(as_bf16x8(xk[kk % 3]), qb[kk], s);
+      dp = mfma32x32x16(as_bf16x8(xv[kk % 3]), gb[kk], dp);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -246,8 +263,8 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(BackwardArgs a) {
     for (int r = 0; r < 16; ++r) dqa[db][r] = 0.f;
 
   if (n > 0) {
-    tile_to_lds(KV[0], kp, koff, a.ks2, tile_at(0) * BC);
-    tile_to_lds(KV[2], vp, voff, a.vs2, tile_at(0) * BC);
+    tile_to_lds(Ks[0], kp, koff, a.ks2, tile_at(0) * BC);
+    tile_to_lds(Vs[0], vp, voff, a.vs2, tile_at(0) * BC);
   }
   auto step = [&](auto PAR, int idx) __attribute__((always_inline)) {
     constexpr int P = decltype(PAR)::value;
@@ -255,17 +272,18 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(BackwardArgs a) {
     __syncthreads();  // tile idx is in LDS; every wave is done with tile idx-1
     if (idx + 1 < n) {
       const int cn = tile_at(idx + 1) * BC;
-      tile_to_lds(KV[P ^ 1], kp, koff, a.ks2, cn);
-      tile_to_lds(KV[2 + (P ^ 1)], vp, voff, a.vs2, cn);
+      tile_to_lds(Ks[P ^ 1], kp, koff, a.ks2, cn);
+      tile_to_lds(Vs[P ^ 1], vp, voff, a.vs2, cn);
     }
     const int c0 = tile_at(idx) * BC;
     const bool edge = (c0 + BC > a.Nk) || (a.causal && c0 + BC - 1 > first_pos);
-    const char* kt = KV[P];
+    const char* kt = Ks[P];
+    const char* vt = Vs[P];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       // S^T and dP^T for keys 32kb..32kb+31 (V tile at the same offset in Vs)
       f32x16_t s, dp;
-      scores2(kt + 8192 * kb, s, dp);
+      scores2(kt + 8192 * kb, vt + 8192 * kb, s, dp);
       if (edge) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {

@@ -27,6 +27,8 @@
 //                           waves sweep independently and only OR their votes
 //                           into an LDS byte per tile; the map row is written
 //                           after one barrier.
+#include <type_traits>
+
 #include "common.hpp"
 
 namespace blasst {
@@ -115,8 +117,13 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
   // Codes of key r (64 bytes, four 16-byte chunks) sit at r * 64 with chunk c
   // stored at position c ^ swz(r), so the 16-byte operand reads of 8
   // consecutive keys fall in distinct banks.
-  __shared__ __attribute__((aligned(16))) char kbuf[2][TPS][BC * ROWB];
-  __shared__ __attribute__((aligned(16))) uint32_t sbuf[2][TPS][BC];
+  // The two stage buffers are separate LDS arrays: the compiler tracks copies
+  // into LDS per array, so reading one buffer does not wait for the copy in
+  // flight into the other.
+  __shared__ __attribute__((aligned(16))) char kbuf0[TPS][BC * ROWB];
+  __shared__ __attribute__((aligned(16))) char kbuf1[TPS][BC * ROWB];
+  __shared__ __attribute__((aligned(16))) uint32_t sbuf0[TPS][BC];
+  __shared__ __attribute__((aligned(16))) uint32_t sbuf1[TPS][BC];
   __shared__ uint8_t flag[kPrefillMaxSetTiles];
 
   const int t = threadIdx.x;
@@ -170,18 +177,26 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
   // that tile's 64 scale words. Keys past Nk repeat the last key.
   const int ckey = 16 * w + (lane >> 2);
   const int cchunk = (lane & 3) ^ swz_k(ckey);
-  auto issue = [&](int st) __attribute__((always_inline)) {
-    const int buf = st & 1;
+  // stage buffers of parity P (compile time)
+  auto kbuf_of = [&](auto PAR) -> char (&)[TPS][BC * ROWB] {
+    if constexpr (decltype(PAR)::value) return kbuf1; else return kbuf0;
+  };
+  auto sbuf_of = [&](auto PAR) -> uint32_t (&)[TPS][BC] {
+    if constexpr (decltype(PAR)::value) return sbuf1; else return sbuf0;
+  };
+  auto issue = [&](auto PAR, int st) __attribute__((always_inline)) {
+    char (&kbuf)[TPS][BC * ROWB] = kbuf_of(PAR);
+    uint32_t (&sbuf)[TPS][BC] = sbuf_of(PAR);
 #pragma unroll
     for (int u = 0; u < TPS; ++u) {
       const int j = st * TPS + u;
       if (j < J) {
         const int key = min(j * BC + ckey, a.Nk - 1);
-        lds_dma16(kc + (int64_t)key * ROWB + 16 * cchunk, &kbuf[buf][u][w * 1024]);
+        lds_dma16(kc + (int64_t)key * ROWB + 16 * cchunk, &kbuf[u][w * 1024]);
         if (w == (u & 3)) {
           const int skey = min(j * BC + lane, a.Nk - 1);
           __builtin_amdgcn_global_load_lds(ks + (int64_t)skey * 4,
-                                           (__attribute__((address_space(3))) void*)&sbuf[buf][u][0],
+                                           (__attribute__((address_space(3))) void*)&sbuf[u][0],
                                            4, 0, 0);
         }
       }
@@ -199,14 +214,15 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
 
   // S^T of tile u of the stage in buffer buf: keys 32kb + 8(r/4) + 4h + r%4
   // of the tile in register r of s[kb], this lane's row in its column
-  auto scores = [&](int buf, int u, f32x16_t (&s)[2]) __attribute__((always_inline)) {
+  auto scores = [&](const char (&kbuf)[TPS][BC * ROWB], const uint32_t (&sbuf)[TPS][BC], int u,
+                    f32x16_t (&s)[2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t sw = sbuf[buf][u][32 * kb + l32];
+      const uint32_t sw = sbuf[u][32 * kb + l32];
       const int ks0 = (int)((sw >> (8 * h)) & 0xffu);
       const int ks1 = (int)((sw >> (16 + 8 * h)) & 0xffu);
-      const u32x4_t k0 = *(const u32x4_t*)&kbuf[buf][u][aoff[kb][0]];
-      const u32x4_t k1 = *(const u32x4_t*)&kbuf[buf][u][aoff[kb][1]];
+      const u32x4_t k0 = *(const u32x4_t*)&kbuf[u][aoff[kb][0]];
+      const u32x4_t k1 = *(const u32x4_t*)&kbuf[u][aoff[kb][1]];
       f32x16_t acc;
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[r] = 0.f;
@@ -241,25 +257,34 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
     m = fmaxf(m, mt);
   };
 
-  issue(0);
-  for (int st = 0; st < nstage; ++st) {
+  const std::integral_constant<int, 0> even;
+  const std::integral_constant<int, 1> odd;
+  auto stage = [&](auto PAR, int st) __attribute__((always_inline)) {
     wait_vmem();
     __syncthreads();  // stage st landed; every wave is done with stage st - 1
-    if (st + 1 < nstage) issue(st + 1);
-    const int buf = st & 1;
+    if (st + 1 < nstage) {
+      if constexpr (decltype(PAR)::value) issue(even, st + 1); else issue(odd, st + 1);
+    }
+    const char (&kbuf)[TPS][BC * ROWB] = kbuf_of(PAR);
+    const uint32_t (&sbuf)[TPS][BC] = sbuf_of(PAR);
     const int j0 = st * TPS;
     // the next tile's MFMAs are issued before this tile's reduction
     f32x16_t sa[2], sb[2];
-    scores(buf, 0, sa);
+    scores(kbuf, sbuf, 0, sa);
 #pragma unroll
     for (int u = 0; u < TPS; u += 2) {
       if (j0 + u >= J) break;
-      if (j0 + u + 1 < J) scores(buf, u + 1, sb);
+      if (j0 + u + 1 < J) scores(kbuf, sbuf, u + 1, sb);
       decide(j0 + u, sa);
       if (j0 + u + 1 >= J) break;
-      if (u + 2 < TPS && j0 + u + 2 < J) scores(buf, u + 2, sa);
+      if (u + 2 < TPS && j0 + u + 2 < J) scores(kbuf, sbuf, u + 2, sa);
       decide(j0 + u + 1, sb);
     }
+  };
+  issue(even, 0);
+  for (int st = 0; st < nstage; st += 2) {
+    stage(even, st);
+    if (st + 1 < nstage) stage(odd, st + 1);
   }
   __syncthreads();
 

@@ -48,7 +48,6 @@ constexpr int BR = 128;   // query tile of the forward mask
 constexpr int BC = 64;    // key tile of the forward mask
 constexpr int NT = 256;
 constexpr int KTILE = BC * D * 2;  // 16 KB: 64 rows x 256 B
-constexpr int QTILE = BR * D * 2;  // 32 KB: 128 rows x 256 B
 constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format, raw access
 
 // XOR applied to the 16-byte chunk index of tile row `row` (depends on row % 16)

@@ -17,16 +17,19 @@
 //                           E2M1 (nearest, ties to the even code, clamped at 6),
 //                           the sign copied; 16 code bytes and one scale byte.
 //   twopass_map_kernel      one workgroup of 4 waves per (batch, query head,
-//                           128-row query tile), wave w owning rows 32w..32w+31.
-//                           S^T = K Q^T per 64-key tile on two scaled
-//                           32x32x64 FP4 MFMAs per 32-key half (lane = query
-//                           row, as in the bf16 prefill), K codes loaded from
-//                           global memory one tile ahead. The running max of a
-//                           row is the prefix max of all earlier tile maxima (a
+//                           pair of 128-row query tiles), waves 0-1 on the
+//                           first tile and 2-3 on the second, each wave owning
+//                           64 rows as two 32-row blocks that share every K
+//                           operand read. S^T = K Q^T per 64-key tile on two
+//                           scaled 32x32x64 FP4 MFMAs per 32-key half and row
+//                           block (lane = query row, as in the bf16 prefill);
+//                           K codes and scales are staged in LDS four tiles at
+//                           a time, double-buffered. The running max of a row
+//                           is the prefix max of all earlier tile maxima (a
 //                           dropped tile cannot raise it when lambda <= 1), so
 //                           waves sweep independently and only OR their votes
-//                           into an LDS byte per tile; the map row is written
-//                           after one barrier.
+//                           into a bit per tile; the map rows are written after
+//                           one barrier.
 #include <type_traits>
 
 #include "common.hpp"
@@ -39,6 +42,7 @@ constexpr int BR = 128;  // query tile
 constexpr int BC = 64;   // key tile
 constexpr int ROWB = 64; // code bytes per row (d = 128)
 constexpr int TPS = 4;   // key tiles per LDS stage of the map kernel
+constexpr int kBufferFlags = 0x00020000;  // buffer resource word 3: 32-bit data format, raw access
 typedef __attribute__((__vector_size__(8 * sizeof(int)))) int i32x8_t;
 
 // E2M1 code (magnitude index 0..7) of a >= 0: nearest of 0, .5, 1, 1.5, 2, 3,
@@ -113,18 +117,18 @@ __global__ void __launch_bounds__(NT) mx_quantize_fp4_kernel(MxQuantArgs a) {
 }
 
 __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
-  // K codes and scales of TPS consecutive key tiles per stage, two stages.
+  // K codes and scales of TPS consecutive key tiles per stage, two stages,
+  // each buffer its own LDS array (copies into LDS are tracked per array, so
+  // reading one stage does not wait for the copy in flight into the other).
   // Codes of key r (64 bytes, four 16-byte chunks) sit at r * 64 with chunk c
   // stored at position c ^ swz(r), so the 16-byte operand reads of 8
   // consecutive keys fall in distinct banks.
-  // The two stage buffers are separate LDS arrays: the compiler tracks copies
-  // into LDS per array, so reading one buffer does not wait for the copy in
-  // flight into the other.
   __shared__ __attribute__((aligned(16))) char kbuf0[TPS][BC * ROWB];
   __shared__ __attribute__((aligned(16))) char kbuf1[TPS][BC * ROWB];
   __shared__ __attribute__((aligned(16))) uint32_t sbuf0[TPS][BC];
   __shared__ __attribute__((aligned(16))) uint32_t sbuf1[TPS][BC];
-  __shared__ uint8_t flag[kPrefillMaxSetTiles];
+  // keep flags of the pair's two query tiles, one bit per key tile
+  __shared__ uint32_t flagw[2][kPrefillMaxSetTiles / 32];
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -132,52 +136,89 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
-  // block -> (query tile, batch, head), as in the bf16 prefill: units of one
-  // (batch, KV head, query tile), heaviest query tiles first, the G query heads
+  // block -> (query-tile pair, batch, head): units of one (batch, KV head,
+  // pair of consecutive query tiles), heaviest pairs first, the G query heads
   // of a unit in G consecutive slots of one XCD (block x runs on XCD x % 8, as
   // its slot x / 8 there); blocks past the last unit return at once
   const int G = a.Hq / a.Hkv;
   const int ngrp = a.B * a.Hkv;
+  const int npair = (a.nqt + 1) >> 1;
   const int slot = (int)(blockIdx.x >> 3);
   const int64_t u = (int64_t)(slot / G) * 8 + (blockIdx.x & 7);
-  if (u >= (int64_t)ngrp * a.nqt) return;
-  const int i = a.nqt - 1 - (int)(u / ngrp);
+  if (u >= (int64_t)ngrp * npair) return;
+  const int ip = npair - 1 - (int)(u / ngrp);
   const int grp = (int)(u % ngrp);
   const int b = grp / a.Hkv, kvh = grp % a.Hkv;
   const int hq = kvh * G + slot % G;
   const int bh = b * a.Hq + hq;
 
-  const int row = i * BR + 32 * w + l32;
-  const bool valid = row < a.Nq;
-  const int qpos = row + (a.Nk - a.Nq);
-  const int last_row = min(i * BR + BR - 1, a.Nq - 1);
-  const int first_pos = i * BR + (a.Nk - a.Nq);
-  const int J = a.causal ? min(a.nkt, (last_row + a.Nk - a.Nq) / BC + 1) : a.nkt;
-  const int nstage = (J + TPS - 1) / TPS;
+  // key tiles visited by query tile qt (all of them when not causal)
+  auto visited = [&](int qt) -> int {
+    const int last_row = min(qt * BR + BR - 1, a.Nq - 1);
+    return a.causal ? min(a.nkt, (last_row + a.Nk - a.Nq) / BC + 1) : a.nkt;
+  };
+  const int i0 = 2 * ip;                      // the pair's first query tile
+  const bool two = i0 + 1 < a.nqt;            // the pair has a second tile
+  const int Jt0 = visited(i0);
+  const int Jt1 = two ? visited(i0 + 1) : 0;
+  const int Jwg = max(Jt0, Jt1);
+  const int nstage = (Jwg + TPS - 1) / TPS;
 
-  for (int x = t; x < J; x += NT) flag[x] = 0;
+  // this wave: query tile i0 + w / 2, rows 64 (w % 2) .. +63 of it as two
+  // 32-row blocks rb, one row per lane column in each
+  const int tw = w >> 1;
+  const int qi = i0 + tw;
+  const bool tile_ok = tw == 0 || two;
+  const int Jw = tw == 0 ? Jt0 : Jt1;        // 0 for a missing second tile
+  const int first_pos = qi * BR + (a.Nk - a.Nq);
+  int row[2], qpos[2];
+  bool valid[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    row[rb] = qi * BR + 64 * (w & 1) + 32 * rb + l32;
+    valid[rb] = tile_ok && row[rb] < a.Nq;
+    qpos[rb] = row[rb] + (a.Nk - a.Nq);
+  }
+
+  for (int x = t; x < 2 * (kPrefillMaxSetTiles / 32); x += NT) (&flagw[0][0])[x] = 0u;
 
   // Q^T as the B operand: lane (row, h) supplies features 64kk + 32h .. +31,
   // i.e. code bytes 32kk + 16h .. +15, with the scale of feature block 2kk + h
-  const int64_t qrow = (int64_t)bh * a.Nq + min(row, a.Nq - 1);
-  const uint8_t* qp = a.qc + qrow * ROWB;
-  const i32x8_t qb0 = operand(load16(qp + 16 * h));
-  const i32x8_t qb1 = operand(load16(qp + 32 + 16 * h));
-  const uint32_t qsw = *(const uint32_t*)(a.qs + qrow * 4);
-  const int qs0 = (int)((qsw >> (8 * h)) & 0xffu);
-  const int qs1 = (int)((qsw >> (16 + 8 * h)) & 0xffu);
+  i32x8_t qb0[2], qb1[2];
+  int qs0[2], qs1[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int64_t qrow = (int64_t)bh * a.Nq + min(row[rb], a.Nq - 1);
+    const uint8_t* qp = a.qc + qrow * ROWB;
+    qb0[rb] = operand(load16(qp + 16 * h));
+    qb1[rb] = operand(load16(qp + 32 + 16 * h));
+    const uint32_t qsw = *(const uint32_t*)(a.qs + qrow * 4);
+    qs0[rb] = (int)((qsw >> (8 * h)) & 0xffu);
+    qs1[rb] = (int)((qsw >> (16 + 8 * h)) & 0xffu);
+  }
 
   const int64_t kbase = (int64_t)(b * a.Hkv + kvh) * a.Nk;
   const uint8_t* kc = a.kc + kbase * ROWB;
   const uint8_t* ks = a.ks + kbase * 4;
 
-  // Copies of stage st into buffer st & 1: wave w moves the codes of keys
-  // 16w .. 16w + 15 of each tile (lane -> key 16w + lane / 4, physical chunk
-  // lane % 4, fetching the logical chunk stored there); wave (tile % 4) moves
-  // that tile's 64 scale words. Keys past Nk repeat the last key.
+  // Copies of stage st into the buffers of parity st & 1, through a buffer
+  // resource per tile whose size stops at Nk (keys past it read as zero codes
+  // and are masked in the reduction): wave w moves the codes of keys 16w ..
+  // 16w + 15 of each tile (lane -> key 16w + lane / 4, physical chunk lane % 4,
+  // fetching the logical chunk stored there); wave (tile % 4) moves that
+  // tile's 64 scale words.
   const int ckey = 16 * w + (lane >> 2);
   const int cchunk = (lane & 3) ^ swz_k(ckey);
-  // stage buffers of parity P (compile time)
+  const uint32_t kvoff = (uint32_t)(ckey * ROWB + 16 * cchunk);
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto rsrc = [&](const uint8_t* p, int bytes) __attribute__((always_inline)) {
+    const uint64_t tb = (uint64_t)p;
+    const uint64_t ub =
+        ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(tb >> 32)) << 32) |
+        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)tb);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0,
+                                             __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
+  };
   auto kbuf_of = [&](auto PAR) -> char (&)[TPS][BC * ROWB] {
     if constexpr (decltype(PAR)::value) return kbuf1; else return kbuf0;
   };
@@ -188,17 +229,17 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
     char (&kbuf)[TPS][BC * ROWB] = kbuf_of(PAR);
     uint32_t (&sbuf)[TPS][BC] = sbuf_of(PAR);
 #pragma unroll
-    for (int u = 0; u < TPS; ++u) {
-      const int j = st * TPS + u;
-      if (j < J) {
-        const int key = min(j * BC + ckey, a.Nk - 1);
-        lds_dma16(kc + (int64_t)key * ROWB + 16 * cchunk, &kbuf[u][w * 1024]);
-        if (w == (u & 3)) {
-          const int skey = min(j * BC + lane, a.Nk - 1);
-          __builtin_amdgcn_global_load_lds(ks + (int64_t)skey * 4,
-                                           (__attribute__((address_space(3))) void*)&sbuf[u][0],
-                                           4, 0, 0);
-        }
+    for (int uu = 0; uu < TPS; ++uu) {
+      const int j = st * TPS + uu;
+      if (j < Jwg) {
+        const int keys = min(a.Nk - j * BC, BC);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc(kc + (int64_t)j * BC * ROWB, keys * ROWB),
+            (__attribute__((address_space(3))) void*)&kbuf[uu][wu * 1024], 16, kvoff, 0, 0, 0);
+        if (wu == (uu & 3))
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rsrc(ks + (int64_t)j * BC * 4, keys * 4),
+              (__attribute__((address_space(3))) void*)&sbuf[uu][0], 4, 4 * lane, 0, 0, 0);
       }
     }
   };
@@ -212,49 +253,59 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
     for (int kk = 0; kk < 2; ++kk) aoff[kb][kk] = key * ROWB + 16 * ((2 * kk + h) ^ swz_k(key));
   }
 
-  // S^T of tile u of the stage in buffer buf: keys 32kb + 8(r/4) + 4h + r%4
-  // of the tile in register r of s[kb], this lane's row in its column
-  auto scores = [&](const char (&kbuf)[TPS][BC * ROWB], const uint32_t (&sbuf)[TPS][BC], int u,
-                    f32x16_t (&s)[2]) __attribute__((always_inline)) {
+  // S^T of tile uu of a stage for both row blocks: keys 32kb + 8(r/4) + 4h +
+  // r%4 of the tile in register r of s[rb][kb], the lane's row of block rb in
+  // its column; each K operand read feeds both row blocks
+  auto scores = [&](const char (&kbuf)[TPS][BC * ROWB], const uint32_t (&sbuf)[TPS][BC], int uu,
+                    f32x16_t (&s)[2][2]) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const uint32_t sw = sbuf[u][32 * kb + l32];
+      const uint32_t sw = sbuf[uu][32 * kb + l32];
       const int ks0 = (int)((sw >> (8 * h)) & 0xffu);
       const int ks1 = (int)((sw >> (16 + 8 * h)) & 0xffu);
-      const u32x4_t k0 = *(const u32x4_t*)&kbuf[u][aoff[kb][0]];
-      const u32x4_t k1 = *(const u32x4_t*)&kbuf[u][aoff[kb][1]];
-      f32x16_t acc;
+      const u32x4_t k0 = *(const u32x4_t*)&kbuf[uu][aoff[kb][0]];
+      const u32x4_t k1 = *(const u32x4_t*)&kbuf[uu][aoff[kb][1]];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[r] = 0.f;
-      acc = mfma_fp4(operand(k0), ks0, qb0, qs0, acc);
-      s[kb] = mfma_fp4(operand(k1), ks1, qb1, qs1, acc);
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x16_t acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        acc = mfma_fp4(operand(k0), ks0, qb0[rb], qs0[rb], acc);
+        s[rb][kb] = mfma_fp4(operand(k1), ks1, qb1[rb], qs1[rb], acc);
+      }
     }
   };
 
-  float m = kNegInf;  // prefix max of this row's tile maxima (raw q.k units)
-  // tile j: row max over visible keys, the row's vote, the workgroup flag
-  auto decide = [&](int j, f32x16_t (&s)[2]) __attribute__((always_inline)) {
+  float m[2] = {kNegInf, kNegInf};  // prefix max of each row's tile maxima (raw q.k units)
+  // tile j: row max over visible keys, the rows' votes, the tile's flag bit
+  auto decide = [&](int j, f32x16_t (&s)[2][2]) __attribute__((always_inline)) {
     const int c0 = j * BC;
     if (c0 + BC > a.Nk || (a.causal && c0 + BC - 1 > first_pos)) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int col = c0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (col >= a.Nk || (a.causal && col > qpos)) s[kb][r] = kNegInf;
-        }
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int col = c0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
+            if (col >= a.Nk || (a.causal && col > qpos[rb])) s[rb][kb][r] = kNegInf;
+          }
     }
-    float mt = kNegInf;
+    bool keep = false;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mt = fmaxf(fmaxf(mt, s[0][r]), s[1][r]);
-    mt = max_with_lane_xor32(mt);
-    // keep unless the gap is below the threshold; a row with no visible key
-    // has gap -inf, and a row with no running max yet has gap +inf (mt - m
-    // is +inf when m = -inf and mt is finite; no NaN can arise)
-    const float gap = mt == kNegInf ? kNegInf : mt - m;
-    const bool keep = valid && !(gap < a.thr_raw);
-    if (__ballot(keep) != 0ull && lane == 0) flag[j] = 1;
-    m = fmaxf(m, mt);
+    for (int rb = 0; rb < 2; ++rb) {
+      float mt = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mt = fmaxf(fmaxf(mt, s[rb][0][r]), s[rb][1][r]);
+      mt = max_with_lane_xor32(mt);
+      // keep unless the gap is below the threshold; a row with no visible key
+      // has gap -inf, and a row with no running max yet has gap +inf (mt - m
+      // is +inf when m = -inf and mt is finite; no NaN can arise)
+      const float gap = mt == kNegInf ? kNegInf : mt - m[rb];
+      keep |= valid[rb] && !(gap < a.thr_raw);
+      m[rb] = fmaxf(m[rb], mt);
+    }
+    if (__ballot(keep) != 0ull && lane == 0) atomicOr(&flagw[tw][j >> 5], 1u << (j & 31));
   };
 
   const std::integral_constant<int, 0> even;
@@ -268,17 +319,16 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
     const char (&kbuf)[TPS][BC * ROWB] = kbuf_of(PAR);
     const uint32_t (&sbuf)[TPS][BC] = sbuf_of(PAR);
     const int j0 = st * TPS;
-    // the next tile's MFMAs are issued before this tile's reduction
-    f32x16_t sa[2], sb[2];
-    scores(kbuf, sbuf, 0, sa);
 #pragma unroll
-    for (int u = 0; u < TPS; u += 2) {
-      if (j0 + u >= J) break;
-      if (j0 + u + 1 < J) scores(kbuf, sbuf, u + 1, sb);
-      decide(j0 + u, sa);
-      if (j0 + u + 1 >= J) break;
-      if (u + 2 < TPS && j0 + u + 2 < J) scores(kbuf, sbuf, u + 2, sa);
-      decide(j0 + u + 1, sb);
+    for (int uu = 0; uu < TPS; ++uu) {
+      if (j0 + uu >= Jw) break;  // past this wave's query tile (uniform)
+      f32x16_t sc[2][2];
+      scores(kbuf, sbuf, uu, sc);
+      decide(j0 + uu, sc);
+      // one tile's scores live at a time; the other waves on the SIMD (three
+      // per SIMD at this register count) overlap one wave's reduction with
+      // another's MFMAs
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
   issue(even, 0);
@@ -288,20 +338,26 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
   }
   __syncthreads();
 
-  // the map row: tile 0 always kept, tiles past the causal bound not visited
-  uint8_t* mrow = a.map + ((int64_t)bh * a.nqt + i) * a.nkt;
+  // the map rows: tile 0 always kept, tiles past the causal bound not visited
   int kept = 0;
-  for (int x = t; x < a.nkt; x += NT) {
-    const uint8_t v = x >= J ? 2 : ((x == 0 || flag[x]) ? 1 : 0);
-    mrow[x] = v;
-    kept += v == 1;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    if (tt == 1 && !two) break;
+    const int Jt = tt == 0 ? Jt0 : Jt1;
+    uint8_t* mrow = a.map + ((int64_t)bh * a.nqt + i0 + tt) * a.nkt;
+    for (int x = t; x < a.nkt; x += NT) {
+      const uint8_t v =
+          x >= Jt ? 2 : ((x == 0 || ((flagw[tt][x >> 5] >> (x & 31)) & 1u)) ? 1 : 0);
+      mrow[x] = v;
+      kept += v == 1;
+    }
   }
   if (a.stats) {
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) kept += __shfl_xor(kept, o, 64);
     if (lane == 0) {
       atomicAdd((unsigned long long*)&a.stats[2 * bh + 1], (unsigned long long)kept);
-      if (w == 0) atomicAdd((unsigned long long*)&a.stats[2 * bh], (unsigned long long)J);
+      if (w == 0) atomicAdd((unsigned long long*)&a.stats[2 * bh], (unsigned long long)(Jt0 + Jt1));
     }
   }
 }
@@ -315,8 +371,9 @@ hipError_t launch_mx_quantize_fp4(const MxQuantArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_twopass_map(const TwoPassMapArgs& a, hipStream_t stream) {
-  // whole rounds of 8 units (one per XCD), G blocks per unit
-  const int64_t units = (int64_t)a.B * a.Hkv * a.nqt;
+  // units of one (batch, KV head, query-tile pair): whole rounds of 8 units
+  // (one per XCD), G blocks per unit
+  const int64_t units = (int64_t)a.B * a.Hkv * ((a.nqt + 1) / 2);
   const int64_t nblocks = (units + 7) / 8 * 8 * (a.Hq / a.Hkv);
   if (units == 0) return hipSuccess;
   hipLaunchKernelGGL(twopass_map_kernel, dim3((unsigned)nblocks), dim3(NT), 0, stream, a);

@@ -294,6 +294,16 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(BackwardArgs a) {
       // 16c + 8(e/4) + 4h + e%4
 #pragma unroll
       for (int cl = 0; cl < 2; ++cl) {
+        // this chunk's K^T reads first, so the dS math covers their latency
+        const int c = 2 * kb + cl;
+        u32x4_t ka[4];
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const u32x2_t y0 = ds_read_tr(kt + 4096 * c + tro[db][0]);
+          const u32x2_t y1 = ds_read_tr(kt + 4096 * c + tro[db][1]);
+          ka[db] = (u32x4_t){y0[0], y0[1], y1[0], y1[1]};
+        }
+        __builtin_amdgcn_sched_barrier(0);
         uint32_t pw[4];
 #pragma unroll
         for (int e2 = 0; e2 < 4; ++e2) {
@@ -304,14 +314,6 @@ __global__ void __launch_bounds__(NT, 2) bwd_dq_kernel(BackwardArgs a) {
         }
         const bf16x8_t pb = as_bf16x8((u32x4_t){pw[0], pw[1], pw[2], pw[3]});
         // dQ^T += K^T dS^T over this 16-key chunk: 4 independent output blocks
-        const int c = 2 * kb + cl;
-        u32x4_t ka[4];
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const u32x2_t y0 = ds_read_tr(kt + 4096 * c + tro[db][0]);
-          const u32x2_t y1 = ds_read_tr(kt + 4096 * c + tro[db][1]);
-          ka[db] = (u32x4_t){y0[0], y0[1], y1[0], y1[1]};
-        }
 #pragma unroll
         for (int db = 0; db < 4; ++db) dqa[db] = mfma32x32x16(as_bf16x8(ka[db]), pb, dqa[db]);
         __builtin_amdgcn_sched_barrier(0);
@@ -523,14 +525,22 @@ __global__ void __launch_bounds__(NT, 2) bwd_kv_kernel(BackwardArgs a) {
         f32x16_t s, dp;
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
+        // operands read two steps ahead (a three-deep register ring)
+        u32x4_t xq[3], xg[3];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          xq[kk] = *(const u32x4_t*)(qt + aro[kk]);
+          if constexpr (DK) xg[kk] = *(const u32x4_t*)(gt + aro[kk]);
+        }
 #pragma unroll
         for (int kk = 0; kk < D / 16; ++kk) {
-          const u32x4_t xq = *(const u32x4_t*)(qt + aro[kk]);
-          s = mfma32x32x16(as_bf16x8(xq), kb[kk], s);
-          if constexpr (DK) {
-            const u32x4_t xg = *(const u32x4_t*)(gt + aro[kk]);
-            dp = mfma32x32x16(as_bf16x8(xg), vb[kk], dp);
+          if (kk + 2 < D / 16) {
+            xq[(kk + 2) % 3] = *(const u32x4_t*)(qt + aro[kk + 2]);
+            if constexpr (DK) xg[(kk + 2) % 3] = *(const u32x4_t*)(gt + aro[kk + 2]);
           }
+          s = mfma32x32x16(as_bf16x8(xq[kk % 3]), kb[kk], s);
+          if constexpr (DK) dp = mfma32x32x16(as_bf16x8(xg[kk % 3]), vb[kk], dp);
+          __builtin_amdgcn_sched_barrier(0);
         }
         if (edge) {
 #pragma unroll
@@ -545,6 +555,14 @@ __global__ void __launch_bounds__(NT, 2) bwd_kv_kernel(BackwardArgs a) {
         const char* bt = DK ? qt : gt;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
+          // this step's transposing reads first, so the P or dS math covers them
+          u32x2_t ya[4][2];
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            ya[db][0] = ds_read_tr(bt + 4096 * ks + tro[db][0]);
+            ya[db][1] = ds_read_tr(bt + 4096 * ks + tro[db][1]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
           uint32_t pw[4];
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
@@ -567,12 +585,10 @@ __global__ void __launch_bounds__(NT, 2) bwd_kv_kernel(BackwardArgs a) {
           }
           const u32x4_t pa = {pw[0], pw[1], pw[2], pw[3]};
 #pragma unroll
-          for (int db = 0; db < 4; ++db) {
-            const u32x2_t y0 = ds_read_tr(bt + 4096 * ks + tro[db][0]);
-            const u32x2_t y1 = ds_read_tr(bt + 4096 * ks + tro[db][1]);
-            acc[db] = mfma32x32x16(as_bf16x8(pa), as_bf16x8((u32x4_t){y0[0], y0[1], y1[0], y1[1]}),
-                                   acc[db]);
-          }
+          for (int db = 0; db < 4; ++db)
+            acc[db] = mfma32x32x16(
+                as_bf16x8(pa),
+                as_bf16x8((u32x4_t){ya[db][0][0], ya[db][0][1], ya[db][1][0], ya[db][1][1]}), acc[db]);
         }
       }
     };

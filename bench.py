@@ -96,8 +96,9 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the prefill backward leg")
     ap.add_argument("--no-twopass", action="store_true", help="skip the two-pass prefill leg")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle sample budget")
-    ap.add_argument("--only", choices=["prefill", "prefill_masked", "backward", "twopass", "decode_gqa",
-                                       "decode_gqa_b1", "decode_mla", "copy"],
+    ap.add_argument("--only", choices=["prefill", "prefill_masked", "backward", "twopass",
+                                       "twopass_skip", "decode_gqa", "decode_gqa_b1", "decode_mla",
+                                       "copy"],
                     help="launch only this kernel --steps times (for rocprofv3 counter passes)")
     ap.add_argument("--workload", choices=["qwen7b", "llama8b"], default="qwen7b",
                     help="prefill layer of --only prefill: the 131072-long Qwen2.5-7B shape or "
@@ -560,15 +561,22 @@ def only(args):
         torch.cuda.synchronize()
         log(f"[bench] copied {n} bytes x {args.steps}")
         return
-    if args.only == "twopass":
-        w = synth.WORKLOADS[2]
-        inp = synth.make_inputs(w.with_gain(6.0))
+    if args.only in ("twopass", "twopass_skip"):
+        # the Llama-shaped layer at gain 6, lambda 1e-2; or the headline layer's
+        # low-needle input at gain 8, lambda 1e-3 (the skip regime)
+        if args.only == "twopass":
+            w, gain, lam = synth.WORKLOADS[2], 6.0, 1e-2
+        else:
+            w, gain, lam = skip_regime_workload(synth.WORKLOADS[HEADLINE_CFG]), 8.0, 1e-3
+        inp = synth.make_inputs(w.with_gain(gain))
         q, k, v = (to_device(x, w) for x in (inp.q, inp.k, inp.v))
         del inp
+        ws = torch.empty(A.prefill_twopass_workspace_size(w.B, w.Hq, w.Hkv, w.Nq, w.Nk),
+                         dtype=torch.uint8, device="cuda")
         for _ in range(args.steps):
-            A.prefill_twopass(q, k, v, 1e-2, causal=True)
+            A.prefill_twopass(q, k, v, lam, causal=True, workspace=ws)
         torch.cuda.synchronize()
-        log(f"[bench] launched two-pass x {args.steps}")
+        log(f"[bench] launched two-pass ({w.name}, gain {gain}, lambda {lam}) x {args.steps}")
         return
     if args.only == "backward":
         w = synth.WORKLOADS[2]

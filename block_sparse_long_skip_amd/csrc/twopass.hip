@@ -132,7 +132,7 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
 
   const int t = threadIdx.x;
   const int lane = t & 63;
-  const int w = t >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);  // uniform: the wave's tile and bounds are scalars
   const int l32 = lane & 31;
   const int h = lane >> 5;
 
@@ -210,7 +210,9 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
   const int ckey = 16 * w + (lane >> 2);
   const int cchunk = (lane & 3) ^ swz_k(ckey);
   const uint32_t kvoff = (uint32_t)(ckey * ROWB + 16 * cchunk);
-  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int wu = w;
+  // one buffer resource over this KV head's codes and one over its scales;
+  // the tile offset goes into the per-lane offset, so the range check covers it
   auto rsrc = [&](const uint8_t* p, int bytes) __attribute__((always_inline)) {
     const uint64_t tb = (uint64_t)p;
     const uint64_t ub =
@@ -219,6 +221,8 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)ub, (short)0,
                                              __builtin_amdgcn_readfirstlane(bytes), kBufferFlags);
   };
+  const __amdgpu_buffer_rsrc_t krs = rsrc(kc, a.Nk * ROWB);
+  const __amdgpu_buffer_rsrc_t srs = rsrc(ks, a.Nk * 4);
   auto kbuf_of = [&](auto PAR) -> char (&)[TPS][BC * ROWB] {
     if constexpr (decltype(PAR)::value) return kbuf1; else return kbuf0;
   };
@@ -232,14 +236,13 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
     for (int uu = 0; uu < TPS; ++uu) {
       const int j = st * TPS + uu;
       if (j < Jwg) {
-        const int keys = min(a.Nk - j * BC, BC);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc(kc + (int64_t)j * BC * ROWB, keys * ROWB),
-            (__attribute__((address_space(3))) void*)&kbuf[uu][wu * 1024], 16, kvoff, 0, 0, 0);
+            krs, (__attribute__((address_space(3))) void*)&kbuf[uu][wu * 1024], 16,
+            kvoff + (uint32_t)(j * BC * ROWB), 0, 0, 0);
         if (wu == (uu & 3))
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rsrc(ks + (int64_t)j * BC * 4, keys * 4),
-              (__attribute__((address_space(3))) void*)&sbuf[uu][0], 4, 4 * lane, 0, 0, 0);
+              srs, (__attribute__((address_space(3))) void*)&sbuf[uu][0], 4,
+              (uint32_t)(4 * lane + j * BC * 4), 0, 0, 0);
       }
     }
   };
@@ -281,15 +284,20 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
   auto decide = [&](int j, f32x16_t (&s)[2][2]) __attribute__((always_inline)) {
     const int c0 = j * BC;
     if (c0 + BC > a.Nk || (a.causal && c0 + BC - 1 > first_pos)) {
+      // key c0 + cc + 4h of register r (cc = 32kb + 8(r/4) + r%4) is masked
+      // past the sequence or after the row's position: cc > lim, one per-lane
+      // bound per row block against immediate offsets
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb)
+      for (int rb = 0; rb < 2; ++rb) {
+        int lim = a.Nk - 1 - c0;
+        if (a.causal) lim = min(lim, qpos[rb] - c0);
+        lim -= 4 * h;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int col = c0 + 32 * kb + 8 * (r >> 2) + 4 * h + (r & 3);
-            if (col >= a.Nk || (a.causal && col > qpos[rb])) s[rb][kb][r] = kNegInf;
-          }
+          for (int r = 0; r < 16; ++r)
+            if (32 * kb + 8 * (r >> 2) + (r & 3) > lim) s[rb][kb][r] = kNegInf;
+      }
     }
     bool keep = false;
 #pragma unroll
@@ -325,7 +333,7 @@ __global__ void __launch_bounds__(NT) twopass_map_kernel(TwoPassMapArgs a) {
       f32x16_t sc[2][2];
       scores(kbuf, sbuf, uu, sc);
       decide(j0 + uu, sc);
-      // one tile's scores live at a time; the other waves on the SIMD (three
+      // one tile's scores live at a time; the other waves on the SIMD (four
       // per SIMD at this register count) overlap one wave's reduction with
       // another's MFMAs
       __builtin_amdgcn_sched_barrier(0);

@@ -219,6 +219,36 @@ def test_prefill_twopass_llama8b_n32768(lam, gain, out):
         assert res.skip_fraction > 0.05
 
 
+def test_prefill_twopass_qwen7b_n131072_low_needles():
+    """The benchmark's skip-regime two-pass call: the 131072-long layer (28 query
+    heads on 4 KV heads, so seven query heads share each map-kernel unit) with
+    every KV head at 0.1% needles, gain 8, lambda 1e-3. Sampled query tiles of
+    heads in three KV groups against the oracle, and whole-call invariants on
+    the map, which must drop most tiles."""
+    w = synth.WORKLOADS[4].scaled(needle_rate=0.001, needle_rate_range=None).with_gain(8.0)
+    inp = synth.make_inputs(w)
+    res = _twopass(inp, w, 1e-3, "bf16")
+    tally = Tally()
+    cache = {}
+    for (h, i) in sample_qtiles(w, [0, 13, 27], 1, seed=7):
+        kvh = h // w.G
+        if kvh not in cache:
+            kf, vf = synth.to_float(inp.k[0, kvh], w), synth.to_float(inp.v[0, kvh], w)
+            cache = {kvh: (kf, vf, mxfp4_values(kf))}
+        kf, vf, kd = cache[kvh]
+        prefill_twopass_tile_parity(res, inp, w, 1e-3, 0, h, i, tally, kf=kf, vf=vf, kd=kd)
+    m = res.mask.cpu().numpy()
+    nqt, nkt = m.shape[2], m.shape[3]
+    assert (m[..., 0] == 1).all()
+    last_vis = (np.minimum((np.arange(nqt) + 1) * w.br, w.Nq) - 1 + w.Nk - w.Nq) // w.bc
+    assert ((m == 2) == (np.arange(nkt)[None, :] > last_vis[:, None])[None, None]).all()
+    st = res.stats.cpu().numpy()
+    assert np.array_equal(st[..., 0], (m != 2).sum(axis=(2, 3)))
+    assert np.array_equal(st[..., 1], (m == 1).sum(axis=(2, 3)))
+    tally.check(w.dtype, "twopass qwen7b low needles lam=1e-3 g=8", out_bf16=True)
+    assert res.skip_fraction > 0.5
+
+
 def test_prefill_twopass_map_in_workspace_matches():
     """Without mask_out the map lives in the workspace; out, lse and statistics
     are the same bits as with it."""

@@ -44,6 +44,7 @@
 namespace blasst {
 
 namespace {
+typedef __attribute__((__vector_size__(2 * sizeof(float)))) float f32x2_t;
 constexpr int BC = 64;
 constexpr int D = 128;
 constexpr int NW = 4;
@@ -385,18 +386,51 @@ __global__ void __launch_bounds__(256) decode_gqa_merge_kernel(DecodeArgs a, Gqa
   const int unit = b * a.Hkv + hq / a.G;
   const float c2 = a.scale_log2;
   const float* ml = sp.part_ml + row * sp.nsplit * 2;
+  // the splits' (m, l) one per lane, 64 splits at a time; the merged max over
+  // the splits that kept something
   float ms = kNegInf;
-  for (int x = 0; x < sp.nsplit; ++x)
-    if (ml[2 * x + 1] > 0.f) ms = fmaxf(ms, ml[2 * x]);
+  for (int x0 = 0; x0 < sp.nsplit; x0 += 64) {
+    const int x = x0 + lane;
+    if (x < sp.nsplit && ml[2 * x + 1] > 0.f) ms = fmaxf(ms, ml[2 * x]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) ms = fmaxf(ms, shfl_xor_f(ms, d));
+  // each split's weight l 2^((m - ms) c2) (0 for a split that kept nothing,
+  // whose partial output is 0), broadcast from its lane; the partial outputs
+  // are read with no branch between them, in split order
   float L = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int x = 0; x < sp.nsplit; ++x) {
-    const float l = ml[2 * x + 1];
-    if (!(l > 0.f)) continue;
-    const float wl = l * fast_exp2((ml[2 * x] - ms) * c2);
-    const float* po = sp.part_o + (row * sp.nsplit + x) * D + 2 * lane;
-    L += wl;
-    o0 += po[0] * wl;
-    o1 += po[1] * wl;
+  for (int x0 = 0; x0 < sp.nsplit; x0 += 64) {
+    const int x = x0 + lane;
+    float wl = 0.f;
+    if (x < sp.nsplit) {
+      const float l = ml[2 * x + 1];
+      if (l > 0.f) wl = l * fast_exp2((ml[2 * x] - ms) * c2);
+    }
+    const int cnt = min(64, sp.nsplit - x0);
+    const float* po = sp.part_o + (row * sp.nsplit + x0) * D + 2 * lane;
+    int y = 0;
+    for (; y + 8 <= cnt; y += 8) {  // eight loads in flight, then their sums
+      f32x2_t v[8];
+      float wy[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        wy[e] = __shfl(wl, y + e, 64);
+        v[e] = *(const f32x2_t*)(po + (int64_t)(y + e) * D);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        L += wy[e];
+        o0 += v[e][0] * wy[e];
+        o1 += v[e][1] * wy[e];
+      }
+    }
+    for (; y < cnt; ++y) {
+      const float wy = __shfl(wl, y, 64);
+      const f32x2_t v = *(const f32x2_t*)(po + (int64_t)y * D);
+      L += wy;
+      o0 += v[0] * wy;
+      o1 += v[1] * wy;
+    }
   }
   const int64_t ob = b * a.os0 + (int64_t)hq * a.os1 + 2 * lane;
   store_out1(a.out, ob, a.out_f32, o0 / L);

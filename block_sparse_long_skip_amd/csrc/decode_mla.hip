@@ -603,20 +603,53 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(DecodeArgs a, Mla
   const int nsplit = ws.nsplit;
   const float c2 = a.scale_log2;
   const float* ml = ws.part_ml + row * nsplit * 4;
+  // the splits' (m, l, l at the reference max) one per lane, 64 splits at a
+  // time; the merged max over the splits that kept something
   float ms = kNegInf;
-  for (int s = 0; s < nsplit; ++s)
-    if (ml[4 * s + 1] > 0.f) ms = fmaxf(ms, ml[4 * s]);
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const int s = s0 + lane;
+    if (s < nsplit && ml[4 * s + 1] > 0.f) ms = fmaxf(ms, ml[4 * s]);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) ms = fmaxf(ms, shfl_xor_f(ms, d));
+  // each split's weight 2^((m - ms) c2) (0 for a split that kept nothing),
+  // broadcast from its lane; the partial outputs are read with no branch
+  // between them, in split order
   float L = 0.f, Lq = 0.f;
   f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-  for (int s = 0; s < nsplit; ++s) {
-    const float l = ml[4 * s + 1];
-    if (!(l > 0.f)) continue;
-    const float wgt = fast_exp2((ml[4 * s] - ms) * c2);
-    L += l * wgt;
-    Lq += ml[4 * s + 2] * wgt;
-    const float* po = ws.part_o + (row * nsplit + s) * DV + 8 * lane;
-    acc0 += *(const f32x4_t*)po * wgt;
-    acc1 += *(const f32x4_t*)(po + 4) * wgt;
+  for (int s0 = 0; s0 < nsplit; s0 += 64) {
+    const int s = s0 + lane;
+    float wgt = 0.f, lw = 0.f, lqw = 0.f;
+    if (s < nsplit) {
+      const float l = ml[4 * s + 1];
+      if (l > 0.f) {
+        wgt = fast_exp2((ml[4 * s] - ms) * c2);
+        lw = l * wgt;
+        lqw = ml[4 * s + 2] * wgt;
+      }
+    }
+    const int cnt = min(64, nsplit - s0);
+    const float* po = ws.part_o + (row * nsplit + s0) * DV + 8 * lane;
+    auto add = [&](int y, const f32x4_t& v0, const f32x4_t& v1) __attribute__((always_inline)) {
+      const float wy = __shfl(wgt, y, 64);
+      L += __shfl(lw, y, 64);
+      Lq += __shfl(lqw, y, 64);
+      acc0 += v0 * wy;
+      acc1 += v1 * wy;
+    };
+    int y = 0;
+    for (; y + 4 <= cnt; y += 4) {  // four splits' loads in flight, then their sums
+      f32x4_t v[4][2];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[e][0] = *(const f32x4_t*)(po + (int64_t)(y + e) * DV);
+        v[e][1] = *(const f32x4_t*)(po + (int64_t)(y + e) * DV + 4);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) add(y + e, v[e][0], v[e][1]);
+    }
+    for (; y < cnt; ++y)
+      add(y, *(const f32x4_t*)(po + (int64_t)y * DV), *(const f32x4_t*)(po + (int64_t)y * DV + 4));
   }
   const float inv = 1.f / Lq;
   const int64_t ob = b * a.os0 + (int64_t)hq * a.os1 + 8 * lane;
@@ -624,25 +657,27 @@ __global__ void __launch_bounds__(256) decode_mla_merge_kernel(DecodeArgs a, Mla
   store_out4(a.out, ob + 4, a.out_f32, acc1[0] * inv, acc1[1] * inv, acc1[2] * inv, acc1[3] * inv);
   if (a.lse && lane == 0) a.lse[row] = ms * a.scale + logf(L);
   if (a.stats) {
-    // tiles that some query head of the KV head keeps (any head group)
-    const uint8_t* any0 = ws.anyk + (int64_t)(b * a.Hkv + kvh) * ws.ngroups * a.nkt;
-    int cv = 0;
-    for (int j = lane; j < a.nkt; j += 64) {
-      bool any = false;
-      for (int x = 0; x < ws.ngroups; ++x) any |= any0[(int64_t)x * a.nkt + j] != 0;
-      cv += any ? 1 : 0;
-    }
     int kept = 0;
     for (int s = lane; s < nsplit; s += 64) kept += ws.part_kept[row * nsplit + s];
-    for (int d = 32; d >= 1; d >>= 1) {
-      cv += __shfl_xor(cv, d, 64);
-      kept += __shfl_xor(kept, d, 64);
-    }
+    for (int d = 32; d >= 1; d >>= 1) kept += __shfl_xor(kept, d, 64);
     if (lane == 0) {
       int64_t* st = a.stats + row * 3;
       st[0] = a.nkt;
       st[1] = kept;
-      st[2] = cv;
+    }
+    // tiles that some query head of the KV head keeps (any head group): one
+    // count per KV head, taken by the wave of its first query head and written
+    // to all G rows
+    if (hq % a.G == 0) {
+      const uint8_t* any0 = ws.anyk + (int64_t)(b * a.Hkv + kvh) * ws.ngroups * a.nkt;
+      int cv = 0;
+      for (int j = lane; j < a.nkt; j += 64) {
+        bool any = false;
+        for (int x = 0; x < ws.ngroups; ++x) any |= any0[(int64_t)x * a.nkt + j] != 0;
+        cv += any ? 1 : 0;
+      }
+      for (int d = 32; d >= 1; d >>= 1) cv += __shfl_xor(cv, d, 64);
+      for (int x = lane; x < a.G; x += 64) a.stats[(row + x) * 3 + 2] = cv;
     }
   }
 }

@@ -236,6 +236,18 @@ def test_decode_gqa_b1_n65536_split(lam, gain):
         assert res.skip_fraction > 0.3
 
 
+@pytest.mark.parametrize("lam,gain", [(1e-3, 1.0), (1e-2, 6.0)])
+@pytest.mark.parametrize("out", ["bf16", "fp32"])
+def test_decode_gqa_split_many_splits(lam, gain, out):
+    """One sequence with one KV head over 300 key tiles: the split plan makes
+    75 splits of 4 tiles, so the merge walks a second chunk of split partials
+    and a remainder of its eight-at-a-time loop. Every row against the oracle."""
+    w = synth.small_workload("decode", B=1, Hq=4, Hkv=1, Nk=300 * 64, d=128, dtype="bf16", bc=64,
+                             gain=gain, seed=57, window=64)
+    assert A.decode_workspace_size(w.B, w.Hq, w.Hkv, w.Nk, w.d, w.dv, latent=False) > 0
+    _check_decode(w, lam, out=out)
+
+
 # The latent-cache kernel splits the cache over workgroups (one split per
 # tile at these sizes, a few tiles per split at the larger ones) and redoes the
 # splits whose speculative decisions differ from the exact ones; two head

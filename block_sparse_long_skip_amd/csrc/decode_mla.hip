@@ -35,8 +35,10 @@
 //
 // Workgroup layout (4 waves, 64 heads). Per key tile:
 //   * the 64 x 576 tile (72 KB) travels global -> LDS through buffer loads
-//     that write LDS directly (no register staging), double-buffered, the next
-//     tile's copy issued at the top of the current one. The tile is stored in
+//     that write LDS directly (no register staging), double-buffered; the next
+//     tile's 18 copies per wave go out one per two score MFMA steps of the
+//     current tile (issued all at once they stall the wave until the address
+//     unit has taken most of them in). The tile is stored in
 //     1 KB blocks with the 16-byte chunk index XOR-swizzled by the row (see
 //     mla_off) so that both the score operand reads and the transposing value
 //     reads hit distinct banks;
@@ -68,6 +70,9 @@ constexpr int ROWB = DQK * 2;             // 1152 bytes per key row
 constexpr int TILEB = BC * ROWB;          // 73728 bytes per tile
 constexpr int NCH = TILEB / 16;           // 4608 16-byte chunks per tile
 constexpr int DMA_PER_WAVE = NCH / 64 / NW;  // 18 copy instructions per wave per tile
+constexpr int CPR = DQK / 64;             // 9 blocks (copy instructions) per block row
+static_assert(DMA_PER_WAVE == 2 * CPR && KS2 == 2 * DMA_PER_WAVE,
+              "a wave's copies are two block rows, one per two score steps");
 constexpr int PP = BC + 8;                // P^T row pitch (bf16): 144 B
 constexpr int LIST_MAX = 256;             // most tiles per split
 constexpr int TARGET_BLOCKS = 256;        // one workgroup per CU
@@ -110,6 +115,13 @@ template <int... CB>
 __device__ __forceinline__ void copy_block_row(__amdgpu_buffer_rsrc_t rs, char* lds, uint32_t voff,
                                                std::integer_sequence<int, CB...>) {
   (copy_block<CB>(rs, lds, voff), ...);
+}
+
+// c + lo + hi of a pair of bf16 values, in one dot-product instruction
+__device__ __forceinline__ float add_bf16x2(uint32_t w, float c) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, w),
+                                         __builtin_bit_cast(bf16x2_t, 0x3F803F80u), c, false);
 }
 
 // gap of a tile max against a running max, with the conventions of the drop
@@ -354,22 +366,23 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
   }
   // Copies go through a buffer resource per (tile, block row): its range ends
   // at the last key of the cache, and the hardware returns zeros for rows
-  // past it (their scores are masked below and their values meet p = 0).
+  // past it (their scores are masked below and their values meet p = 0). An
+  // empty range (on = false) makes the copies write zeros and read nothing.
+  auto copy_rsrc = [&](int j, int r2, bool on) __attribute__((always_inline)) {
+    // all uniform; readfirstlane tells the compiler so (no waterfall loop)
+    const int row0t = __builtin_amdgcn_readfirstlane(j * BC + 16 * wu + 8 * r2);  // first key
+    const int nrec = on ? __builtin_amdgcn_readfirstlane(min(max(Nk - row0t, 0), 8) * (int)rs32) : 0;
+    const uint64_t base = (uint64_t)(kp + (int64_t)row0t * rowstride);
+    const uint64_t ubase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32)) << 32) |
+                           (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
+    return __builtin_amdgcn_make_buffer_rsrc((void*)ubase, (short)0, nrec, kBufferFlags);
+  };
+  // the whole tile at once (the first tile of the loop)
   auto tile_to_lds = [&](char* tile, int j) __attribute__((always_inline)) {
-    const int c0 = j * BC;
 #pragma unroll
-    for (int r2 = 0; r2 < 2; ++r2) {
-      // all uniform; readfirstlane tells the compiler so (no waterfall loop)
-      const int row0t = __builtin_amdgcn_readfirstlane(c0 + 16 * wu + 8 * r2);  // first key
-      const int nrec = __builtin_amdgcn_readfirstlane(min(max(Nk - row0t, 0), 8) * (int)rs32);
-      const uint64_t base = (uint64_t)(kp + (int64_t)row0t * rowstride);
-      const uint64_t ubase = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(base >> 32)) << 32) |
-                             (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)base);
-      const __amdgpu_buffer_rsrc_t rs =
-          __builtin_amdgcn_make_buffer_rsrc((void*)ubase, (short)0, nrec, kBufferFlags);
-      copy_block_row(rs, tile + 1024 * (DMA_PER_WAVE * wu + (DQK / 64) * r2), loff[r2],
-                     std::make_integer_sequence<int, DQK / 64>{});
-    }
+    for (int r2 = 0; r2 < 2; ++r2)
+      copy_block_row(copy_rsrc(j, r2, true), tile + 1024 * (DMA_PER_WAVE * wu + CPR * r2), loff[r2],
+                     std::make_integer_sequence<int, CPR>{});
   };
 
   f32x16_t o[4][2];  // O^T[dv = 128w + 32db + 8(i/4) + 4h + i%4][head 32hb + l32]
@@ -413,7 +426,12 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
     char* kt = P ? Kt1 : Kt0;
     wait_vmem();
     __syncthreads();  // (C) tile idx is in LDS; every wave is done with tile idx-1
-    if (idx + 1 < nl) tile_to_lds(P ? Kt0 : Kt1, tile_of(idx + 1));
+    // the next tile's copies into the other buffer (every wave is done with
+    // it); after the last tile they write zeros there and read nothing
+    const bool nx = idx + 1 < nl;
+    const int jn = nx ? tile_of(idx + 1) : j;
+    const __amdgpu_buffer_rsrc_t nrs0 = copy_rsrc(jn, 0, nx), nrs1 = copy_rsrc(jn, 1, nx);
+    char* const nb = (P ? Kt0 : Kt1) + 1024 * DMA_PER_WAVE * wu;
 
     // scores S^T[key 32kh + 8(i/4) + 4h + i%4][head hl]: 36 steps on two
     // accumulator chains, each step's K operand read four steps ahead
@@ -427,11 +445,30 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
     for (int kk = 0; kk < KS2; ++kk) {
       const u32x4_t cur = kbuf[kk & 3];
       if (kk + 4 < KS2) kbuf[kk & 3] = *(const u32x4_t*)(kt + ko[kk & 3] + 1024 * ((kk + 4) >> 2));
+      if ((kk & 1) == 0) {
+        // the next tile's copies, one block per two score steps: block c of
+        // the wave's 18 is block c % 9 of block row c / 9
+        const int c = kk >> 1;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            c < CPR ? nrs0 : nrs1, (__attribute__((address_space(3))) void*)(nb + 1024 * c), 16,
+            loff[c < CPR ? 0 : 1], 128 * (c % CPR), 0, 0);
+      }
       if (kk & 1) s1 = mfma32x32x16(as_bf16x8(cur), qb[kk], s1);
       else s0 = mfma32x32x16(as_bf16x8(cur), qb[kk], s0);
       __builtin_amdgcn_sched_barrier(0);
     }
     f32x16_t sc = s0 + s1;
+    // V^T operand reads of one 16-key step of the P.V product
+    auto rdv = [&](int ks, u32x4_t (&va)[4]) __attribute__((always_inline)) {
+      const char* vk = kt + 16 * ks * ROWB;  // two block rows
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const u32x2_t y0 = ds_read_tr(vk + 1024 * (db >> 1) + vo[db & 1][0]);
+        const u32x2_t y1 = ds_read_tr(vk + 1024 * (db >> 1) + vo[db & 1][1]);
+        va[db] = (u32x4_t){y0[0], y0[1], y1[0], y1[1]};
+      }
+    };
+    u32x4_t va0[4];  // the first step's, read while the softmax runs
     const int c0 = j * BC;
     if (c0 + BC > Nk) {
 #pragma unroll
@@ -450,6 +487,7 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
       lds_barrier();  // (A) tile maxima of both key halves visible
 
       const float TM = fmaxf(tmw[P][0][hl], tmw[P][1][hl]);
+      rdv(0, va0);
       const bool sink_only = idx < pre;  // tile 0 scored by a later split: max only
       if (sink_only && hv) m = fmaxf(m, TM);
       if (!sink_only && kh == 0 && h == 0 && hv) tmaxp[(int64_t)j * G + hl] = TM;
@@ -474,13 +512,14 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
           const float p1 = fast_exp2(fmaf(sc[2 * x + 1], c2, -mc));
           lp += p0 + p1;
           pw[x] = pack_bf16x2(p0, p1);
-          lq += bf16_lo(pw[x]) + bf16_hi(pw[x]);
+          lq = add_bf16x2(pw[x], lq);
         }
       }
     } else {
       // correction: this tile was kept by pass 0 for the heads in the mask
       // and is dropped by the exact rule; its contribution at the partial's
       // reference max is subtracted (same p, negated)
+      rdv(0, va0);
       keep = hv && ((lmask[idx] >> hl) & 1ull) != 0ull;
       if (keep) {
         const float mc = m_acc * c2;
@@ -490,7 +529,7 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
           const float p1 = -fast_exp2(fmaf(sc[2 * x + 1], c2, -mc));
           lp += p0 + p1;
           pw[x] = pack_bf16x2(p0, p1);
-          lq += bf16_lo(pw[x]) + bf16_hi(pw[x]);
+          lq = add_bf16x2(pw[x], lq);
         }
       }
     }
@@ -511,36 +550,30 @@ __global__ void __launch_bounds__(NT, 1) decode_mla_split_kernel(DecodeArgs a, M
       }
     }
     if (fl & 1) {
-      // O^T += V^T P^T over 4 steps of 16 keys; each step's operands are read
-      // one step ahead
-      auto rd = [&](int ks, u32x4_t (&va)[4], u32x4_t (&pb)[2]) __attribute__((always_inline)) {
-        const char* vk = kt + 16 * ks * ROWB;  // two block rows
+      // O^T += V^T P^T over 4 steps of 16 keys: every P^T operand read at
+      // once, the V^T operands one step ahead (the first step's before the
+      // barrier)
+      u32x4_t pb[4][2];
 #pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const u32x2_t y0 = ds_read_tr(vk + 1024 * (db >> 1) + vo[db & 1][0]);
-          const u32x2_t y1 = ds_read_tr(vk + 1024 * (db >> 1) + vo[db & 1][1]);
-          va[db] = (u32x4_t){y0[0], y0[1], y1[0], y1[1]};
-        }
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
-          pb[hb] = *(const u32x4_t*)&Ps[(32 * hb + l32) * PP + 16 * ks + 8 * h];
-      };
-      u32x4_t va[4], pb[2];
-      rd(0, va, pb);
+          pb[ks][hb] = *(const u32x4_t*)&Ps[(32 * hb + l32) * PP + 16 * ks + 8 * h];
+      u32x4_t va[4];
+#pragma unroll
+      for (int db = 0; db < 4; ++db) va[db] = va0[db];
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) {
-        u32x4_t van[4], pbn[2];
-        if (ks + 1 < 4) rd(ks + 1, van, pbn);
+        u32x4_t van[4];
+        if (ks + 1 < 4) rdv(ks + 1, van);
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb)
-            o[db][hb] = mfma32x32x16(as_bf16x8(va[db]), as_bf16x8(pb[hb]), o[db][hb]);
+            o[db][hb] = mfma32x32x16(as_bf16x8(va[db]), as_bf16x8(pb[ks][hb]), o[db][hb]);
         if (ks + 1 < 4) {
 #pragma unroll
           for (int db = 0; db < 4; ++db) va[db] = van[db];
-          pb[0] = pbn[0];
-          pb[1] = pbn[1];
         }
         __builtin_amdgcn_sched_barrier(0);
       }

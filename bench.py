@@ -452,7 +452,10 @@ def bench_decode(args):
     from block_sparse_long_skip_amd import synth
 
     results = {}
-    flush = torch.empty(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB, evicts L2 and MALL
+    # Every timed call follows a read of this 1 GiB buffer, which evicts the cache
+    # from L2 and MALL. A read, not a fill: a fill leaves about 300 MB of dirty
+    # lines there, and writing them back (≈40 µs) would be charged to the decode.
+    flush = torch.zeros(1 << 28, dtype=torch.int32, device="cuda")
     # the batch-32 GQA decode, the same layer for a single sequence (its cache
     # split over workgroups), and the batch-16 MLA decode
     for w, kind in ((synth.WORKLOADS[3], "decode_gqa_b32_n65536"),
@@ -475,7 +478,7 @@ def bench_decode(args):
                 # the inputs, and the first calls after that run at a lower clock
                 nwarm = 3
                 for it in range(nwarm + max(3, args.steps // 2)):
-                    flush.fill_(it)
+                    torch.sum(flush)
                     s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                     s.record()
                     res = A.decode(q, k, v, lam, bc=w.bc, dv=w.dv, workspace=ws)

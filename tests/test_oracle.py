@@ -75,7 +75,7 @@ def pin_hand_example(orc):
         want_lse = float(np.log(np.exp(ks).sum()))
         assert abs(r.out[0, 0, 0, 0] - want_out) < 1e-12
         assert abs(r.lse[0, 0, 0] - want_lse) < 1e-12
-    # the survey's printed digits for the first case
+    # the first case's closed form to ten digits: (1 + 3e) / (1 + e)
     assert abs((1 + 3 * math.e) / (1 + math.e) - 2.4621171573) < 1e-10
 
 
